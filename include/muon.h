@@ -1,0 +1,200 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon / AdamW optimizer-step library.
+ *
+ * Sources the operations follow, cited by page title and section:
+ *   [OPT] "Optimizer tutorial" page on mhpq.cn (large-model training series,
+ *         part 2): 2.1 momentum as an EMA of the gradient; 2.3 Adam with
+ *         bias correction; 3.1 AdamW's decoupled weight decay; 3.3 fp32
+ *         master weights cast back to 16 bit; 4.2 the Newton-Schulz
+ *         iteration X <- (3X - X X^T X)/2, run a fixed number of times.
+ *   [K2]  Zhihu answer by toothacher17 on the Kimi K2 release: 2.2 the
+ *         optimizer works on all parameters flattened and concatenated,
+ *         each matrix whole; 3.1 Muon's update RMS is matched to AdamW's;
+ *         3.2 the max(1, sqrt(d_out/d_in)) update scale; 4 the spectral
+ *         norm is bounded by the Frobenius norm.
+ *   [EP]  aihot.vn news item on MoonEP, "memory contract": expert weights
+ *         live in one contiguous [E, H, H'] tensor addressed by row offset.
+ *
+ * Conventions for every call:
+ *   - Returns MUON_OK (0) or a negative MUON_ERR_* code; nothing throws.
+ *     muon_last_error() gives a message for the last failure on the
+ *     calling thread.
+ *   - Device pointers are plain HIP device addresses on the device that was
+ *     current when the plan was created.  All of them are owned by the
+ *     caller; the library keeps no pointer after a call returns.
+ *   - Work is enqueued on the caller's HIP stream; the library never
+ *     synchronises.  A kernel fault surfaces at the caller's next
+ *     synchronisation of that stream.
+ *   - Buffers passed to one call must not alias each other.
+ *   - Non-finite inputs propagate into the outputs; there is no guard.
+ */
+#ifndef MUON_H_
+#define MUON_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define MUON_OK 0
+#define MUON_ERR_INVALID_ARG (-1)        /* null pointer, bad hyperparameter, wrong device */
+#define MUON_ERR_BAD_SHAPE (-2)          /* rows/cols < 1, matrix outside the flat buffer, too large */
+#define MUON_ERR_OVERLAP (-3)            /* two matrices share flat elements */
+#define MUON_ERR_WORKSPACE_TOO_SMALL (-4)
+#define MUON_ERR_BAD_DTYPE (-5)
+#define MUON_ERR_HIP (-6)                /* a HIP runtime call failed; see muon_last_error() */
+#define MUON_ERR_UNSUPPORTED (-7)
+
+/* ---- element types ---------------------------------------------------- */
+#define MUON_DTYPE_FP32 0
+#define MUON_DTYPE_BF16 1
+
+/* One matrix of the flat buffer ([K2] 2.2): elements
+ * [offset, offset + rows*cols) of the flat params / grads / momentum
+ * buffers, row-major [rows, cols].  The same offset addresses all three. */
+typedef struct {
+  int64_t offset;
+  int32_t rows;
+  int32_t cols;
+} muon_matrix_t;
+
+/* Hyperparameters of one Muon step.
+ *   lr, weight_decay : W <- (1 - lr*wd) W - lr*s*O   ([OPT] 3.1 decoupled form)
+ *   momentum (mu)    : M <- mu M + (1-mu) G          ([OPT] 2.1 EMA)
+ *   nesterov         : nonzero: NS input U = mu M + (1-mu) G; zero: U = M
+ *   ns_a, ns_b, ns_c : per NS iteration A = X X^T, B = b A + c A A,
+ *                      X <- a X + B X  ([OPT] 4.2 prints (1.5, -0.5, 0))
+ *   ns_steps         : number of NS iterations (>= 0; [OPT] 4.2: typically 5)
+ *   eps              : X0 = U / (||U||_F + eps)      ([K2] 4)
+ *   scale_mode       : s = rms_target*sqrt(max(r,c)) (0, [K2] 3.1),
+ *                      sqrt(max(1, r/c)) (1, [K2] 3.2), 1 (2)
+ */
+typedef struct {
+  float lr;
+  float weight_decay;
+  float momentum;
+  int32_t nesterov;
+  float ns_a;
+  float ns_b;
+  float ns_c;
+  int32_t ns_steps;
+  float eps;
+  int32_t scale_mode;
+  float rms_target;
+} muon_hparams_t;
+
+/* Hyperparameters of one AdamW step ([OPT] 2.3, 3.1). */
+typedef struct {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+} adamw_hparams_t;
+
+/* Opaque plan: matrix descriptors validated, orientation (tall matrices
+ * are iterated transposed so the Gram matrix is min(r,c) square), padding
+ * to the GEMM tile, workspace layout, tile lists and waves.  Immutable
+ * after creation; the plan owns one small device allocation holding its
+ * tables, freed by muon_plan_destroy. */
+typedef struct muon_plan muon_plan_t;
+
+typedef struct {
+  int32_t n_mats;
+  int32_t n_waves;
+  int32_t tile;               /* GEMM tile edge (256 for bf16 NS, 64 for fp32 NS) */
+  int32_t ns_dtype;
+  int64_t k1_tiles;           /* 64x64 elementwise tiles, all waves */
+  int64_t syrk_tiles;         /* X X^T tiles (one triangle), all waves */
+  int64_t bx_tiles;           /* B X tiles, all waves */
+  size_t workspace_bytes;
+  double ns_flops_per_iter_alg;   /* algorithmic flops per NS iteration with c != 0 */
+} muon_plan_info_t;
+
+/* Host-only sizing: validates exactly as muon_plan_create and returns the
+ * workspace size in bytes.  Makes no HIP call; usable without a GPU.
+ * workspace_cap (bytes, 0 = unlimited) bounds the workspace by splitting
+ * the matrices into waves that run one after another. */
+int muon_workspace_size(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
+                        int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
+                        size_t workspace_cap, size_t* workspace_bytes);
+
+/* Build a plan on the current device.  n_mats may be 0 (steps are then
+ * no-ops).  On success *out owns the plan and *workspace_bytes is the
+ * size of the device workspace every step needs. */
+int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
+                     int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
+                     size_t workspace_cap, muon_plan_t** out, size_t* workspace_bytes);
+
+void muon_plan_destroy(muon_plan_t* plan);
+
+int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info);
+
+/* One Muon step on every matrix of the plan.
+ *   params     : flat, param_dtype, updated in place (bf16 stored RNE)
+ *   grads      : flat, grad_dtype, read only
+ *   momentum   : flat fp32, updated in place
+ *   workspace  : >= workspace_bytes of device memory, 256-byte aligned;
+ *                scratch only, contents on entry are ignored
+ *   out_update : nullable flat fp32; receives O (the orthogonalised update
+ *                before scaling) at each matrix's elements
+ * Elements of the flat buffers not covered by a matrix are never touched.
+ * Concurrent steps on one workspace race; use one workspace per stream. */
+int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* momentum,
+              void* workspace, size_t workspace_bytes, const muon_hparams_t* hp,
+              float* out_update, hipStream_t stream);
+
+/* The stages muon_step enqueues, exposed for stepwise checks and timing.
+ * muon_step(...) == for each wave w: muon_stage_momentum(w);
+ *   for it in [0, ns_steps): for phase in {1, 2 (only if ns_c != 0), 3}:
+ *   muon_stage_ns_phase(w, it, phase); muon_stage_apply(w).
+ * Phase 1: A = X X^T; phase 2: B = b A + c A A; phase 3: X <- a X + B X
+ * (with c == 0, phase 3 uses b A for B). */
+int muon_stage_momentum(const muon_plan_t* plan, int32_t wave, const void* grads,
+                        float* momentum, void* workspace, size_t workspace_bytes,
+                        const muon_hparams_t* hp, hipStream_t stream);
+int muon_stage_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
+                        size_t workspace_bytes, const muon_hparams_t* hp, int32_t iter,
+                        int32_t phase, hipStream_t stream);
+int muon_stage_apply(const muon_plan_t* plan, int32_t wave, void* params, void* workspace,
+                     size_t workspace_bytes, const muon_hparams_t* hp, float* out_update,
+                     hipStream_t stream);
+
+/* Copy the current NS iterate of every matrix of a wave into a flat fp32
+ * buffer at each matrix's elements, in the caller's [rows, cols] layout
+ * (after muon_stage_momentum it is U, the un-normalised NS input).
+ * For stepwise checks. */
+int muon_stage_export_x(const muon_plan_t* plan, int32_t wave, const void* workspace,
+                        size_t workspace_bytes, int32_t iter_done, float* out,
+                        hipStream_t stream);
+/* Copy the per-matrix Frobenius norms ||U||_F of a wave (fp32, one per
+ * matrix of the wave, in plan order) after muon_stage_momentum. */
+int muon_stage_export_norms(const muon_plan_t* plan, int32_t wave, const void* workspace,
+                            size_t workspace_bytes, float* out, hipStream_t stream);
+
+/* One AdamW step ([OPT] 2.3, 3.1, 3.3) over n contiguous elements:
+ *   m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2
+ *   theta <- theta - lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps) - lr wd theta
+ * master non-null: theta is the fp32 master, and params (param_dtype)
+ *   receives its round-to-nearest-even cast.
+ * master null: params must be fp32 and is theta itself.
+ * grads: grad_dtype.  exp_avg, exp_avg_sq: fp32, updated in place.
+ * step: 1-based t; the bias corrections are formed in fp64 on the host.
+ * No alignment is required beyond the element size. */
+int adamw_step(void* params, int32_t param_dtype, float* master, const void* grads,
+               int32_t grad_dtype, float* exp_avg, float* exp_avg_sq, int64_t n,
+               const adamw_hparams_t* hp, int64_t step, hipStream_t stream);
+
+const char* muon_status_string(int32_t status);
+const char* muon_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H_ */

@@ -1,1 +1,286 @@
-"""MI355X-native Muon (Newton-Schulz) and AdamW optimizer step."""
+"""MI355X-native Muon (Newton-Schulz) and AdamW optimizer step.
+
+Thin ctypes binding over ``libmuon.so`` (C ABI in ``include/muon.h``).  The
+functions keep the C names; they only marshal arguments (tensor ->
+device pointer, dtype -> code, current torch stream -> hipStream_t) and
+turn status codes into ``MuonError``.  Every step of the optimizer runs in
+the library's HIP kernels; there is no Python or CPU fallback: if the
+library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmuon.so")
+
+MUON_OK = 0
+MUON_ERR_INVALID_ARG = -1
+MUON_ERR_BAD_SHAPE = -2
+MUON_ERR_OVERLAP = -3
+MUON_ERR_WORKSPACE_TOO_SMALL = -4
+MUON_ERR_BAD_DTYPE = -5
+MUON_ERR_HIP = -6
+MUON_ERR_UNSUPPORTED = -7
+
+MUON_DTYPE_FP32 = 0
+MUON_DTYPE_BF16 = 1
+
+EXPORTED = [
+    "muon_workspace_size", "muon_plan_create", "muon_plan_destroy", "muon_plan_get_info",
+    "muon_step", "muon_stage_momentum", "muon_stage_ns_phase", "muon_stage_apply",
+    "muon_stage_export_x", "muon_stage_export_norms", "adamw_step", "muon_status_string",
+    "muon_last_error",
+]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class MuonMatrix(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class MuonHParamsC(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("momentum", ctypes.c_float), ("nesterov", ctypes.c_int32),
+                ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
+                ("ns_steps", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("scale_mode", ctypes.c_int32), ("rms_target", ctypes.c_float)]
+
+
+class AdamWHParamsC(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
+
+
+class MuonPlanInfo(ctypes.Structure):
+    _fields_ = [("n_mats", ctypes.c_int32), ("n_waves", ctypes.c_int32),
+                ("tile", ctypes.c_int32), ("ns_dtype", ctypes.c_int32),
+                ("k1_tiles", ctypes.c_int64), ("syrk_tiles", ctypes.c_int64),
+                ("bx_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
+                ("ns_flops_per_iter_alg", ctypes.c_double)]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmuon.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m muon_newton_schulz_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    mats_p = ctypes.POINTER(MuonMatrix)
+    L.muon_workspace_size.argtypes = [mats_p, I32, I64, I32, I32, I32, SZ, ctypes.POINTER(SZ)]
+    L.muon_plan_create.argtypes = [mats_p, I32, I64, I32, I32, I32, SZ, ctypes.POINTER(P),
+                                   ctypes.POINTER(SZ)]
+    L.muon_plan_destroy.argtypes = [P]
+    L.muon_plan_destroy.restype = None
+    L.muon_plan_get_info.argtypes = [P, ctypes.POINTER(MuonPlanInfo)]
+    hp_p = ctypes.POINTER(MuonHParamsC)
+    L.muon_step.argtypes = [P, P, P, P, P, SZ, hp_p, P, P]
+    L.muon_stage_momentum.argtypes = [P, I32, P, P, P, SZ, hp_p, P]
+    L.muon_stage_ns_phase.argtypes = [P, I32, P, SZ, hp_p, I32, I32, P]
+    L.muon_stage_apply.argtypes = [P, I32, P, P, SZ, hp_p, P, P]
+    L.muon_stage_export_x.argtypes = [P, I32, P, SZ, I32, P, P]
+    L.muon_stage_export_norms.argtypes = [P, I32, P, SZ, P, P]
+    L.adamw_step.argtypes = [P, I32, P, P, I32, P, P, I64, ctypes.POINTER(AdamWHParamsC), I64, P]
+    L.muon_status_string.argtypes = [I32]
+    L.muon_status_string.restype = ctypes.c_char_p
+    L.muon_last_error.argtypes = []
+    L.muon_last_error.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name not in ("muon_plan_destroy", "muon_status_string", "muon_last_error"):
+            getattr(L, name).restype = ctypes.c_int
+    _lib_handle = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != MUON_OK:
+        msg = lib().muon_last_error().decode(errors="replace")
+        raise MuonError(rc, msg or muon_status_string(rc))
+
+
+def muon_status_string(status: int) -> str:
+    return lib().muon_status_string(status).decode()
+
+
+def muon_last_error() -> str:
+    return lib().muon_last_error().decode(errors="replace")
+
+
+# ---------------------------------------------------------------- marshalling
+
+def dtype_code(dt) -> int:
+    import torch
+    table = {"fp32": MUON_DTYPE_FP32, "bf16": MUON_DTYPE_BF16,
+             torch.float32: MUON_DTYPE_FP32, torch.bfloat16: MUON_DTYPE_BF16}
+    if dt not in table:
+        raise MuonError(MUON_ERR_BAD_DTYPE, f"unsupported dtype {dt}")
+    return table[dt]
+
+
+def _mats_array(mats: Sequence[Tuple[int, int, int]]):
+    arr = (MuonMatrix * max(1, len(mats)))()
+    for k, (o, r, c) in enumerate(mats):
+        arr[k] = MuonMatrix(int(o), int(r), int(c))
+    return arr
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _hp(hp) -> MuonHParamsC:
+    if isinstance(hp, MuonHParamsC):
+        return hp
+    return MuonHParamsC(float(hp.lr), float(hp.weight_decay), float(hp.momentum),
+                        int(bool(hp.nesterov)), float(hp.ns_a), float(hp.ns_b),
+                        float(hp.ns_c), int(hp.ns_steps), float(hp.eps), int(hp.scale_mode),
+                        float(hp.rms_target))
+
+
+def _ahp(hp) -> AdamWHParamsC:
+    if isinstance(hp, AdamWHParamsC):
+        return hp
+    return AdamWHParamsC(float(hp.lr), float(hp.beta1), float(hp.beta2), float(hp.eps),
+                         float(hp.weight_decay))
+
+
+# ---------------------------------------------------------------- plan
+
+class MuonPlan:
+    """Owns a muon_plan_t (destroyed with the object)."""
+
+    def __init__(self, handle: int, workspace_bytes: int, n_mats: int):
+        self.handle = handle
+        self.workspace_bytes = workspace_bytes
+        self.n_mats = n_mats
+
+    def info(self) -> MuonPlanInfo:
+        return muon_plan_get_info(self)
+
+    def alloc_workspace(self, device="cuda"):
+        import torch
+        return torch.empty(max(1, self.workspace_bytes), dtype=torch.uint8, device=device)
+
+    def close(self):
+        if self.handle:
+            lib().muon_plan_destroy(ctypes.c_void_p(self.handle))
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def muon_workspace_size(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype,
+                        workspace_cap: int = 0) -> int:
+    arr = _mats_array(mats)
+    out = ctypes.c_size_t(0)
+    _check(lib().muon_workspace_size(arr, len(mats), int(flat_numel), dtype_code(param_dtype),
+                                     dtype_code(grad_dtype), dtype_code(ns_dtype),
+                                     int(workspace_cap), ctypes.byref(out)))
+    return out.value
+
+
+def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="bf16",
+                     workspace_cap: int = 0) -> MuonPlan:
+    arr = _mats_array(mats)
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+    _check(lib().muon_plan_create(arr, len(mats), int(flat_numel), dtype_code(param_dtype),
+                                  dtype_code(grad_dtype), dtype_code(ns_dtype),
+                                  int(workspace_cap), ctypes.byref(h), ctypes.byref(ws)))
+    return MuonPlan(h.value, ws.value, len(mats))
+
+
+def muon_plan_destroy(plan: MuonPlan) -> None:
+    plan.close()
+
+
+def muon_plan_get_info(plan: MuonPlan) -> MuonPlanInfo:
+    info = MuonPlanInfo()
+    _check(lib().muon_plan_get_info(ctypes.c_void_p(plan.handle), ctypes.byref(info)))
+    return info
+
+
+def muon_step(plan: MuonPlan, params, grads, momentum, workspace, hp, out_update=None,
+              stream=None) -> None:
+    h = _hp(hp)
+    _check(lib().muon_step(ctypes.c_void_p(plan.handle), _ptr(params), _ptr(grads),
+                           _ptr(momentum), _ptr(workspace), workspace.numel(), ctypes.byref(h),
+                           _ptr(out_update), _stream(stream)))
+
+
+def muon_stage_momentum(plan: MuonPlan, wave: int, grads, momentum, workspace, hp,
+                        stream=None) -> None:
+    h = _hp(hp)
+    _check(lib().muon_stage_momentum(ctypes.c_void_p(plan.handle), wave, _ptr(grads),
+                                     _ptr(momentum), _ptr(workspace), workspace.numel(),
+                                     ctypes.byref(h), _stream(stream)))
+
+
+def muon_stage_ns_phase(plan: MuonPlan, wave: int, workspace, hp, iter: int, phase: int,
+                        stream=None) -> None:
+    h = _hp(hp)
+    _check(lib().muon_stage_ns_phase(ctypes.c_void_p(plan.handle), wave, _ptr(workspace),
+                                     workspace.numel(), ctypes.byref(h), iter, phase,
+                                     _stream(stream)))
+
+
+def muon_stage_apply(plan: MuonPlan, wave: int, params, workspace, hp, out_update=None,
+                     stream=None) -> None:
+    h = _hp(hp)
+    _check(lib().muon_stage_apply(ctypes.c_void_p(plan.handle), wave, _ptr(params),
+                                  _ptr(workspace), workspace.numel(), ctypes.byref(h),
+                                  _ptr(out_update), _stream(stream)))
+
+
+def muon_stage_export_x(plan: MuonPlan, wave: int, workspace, iter_done: int, out,
+                        stream=None) -> None:
+    _check(lib().muon_stage_export_x(ctypes.c_void_p(plan.handle), wave, _ptr(workspace),
+                                     workspace.numel(), iter_done, _ptr(out), _stream(stream)))
+
+
+def muon_stage_export_norms(plan: MuonPlan, wave: int, workspace, out, stream=None) -> None:
+    _check(lib().muon_stage_export_norms(ctypes.c_void_p(plan.handle), wave, _ptr(workspace),
+                                         workspace.numel(), _ptr(out), _stream(stream)))
+
+
+def adamw_step(params, master, grads, exp_avg, exp_avg_sq, hp, step: int, stream=None) -> None:
+    """params/grads may be bf16 or fp32 tensors; master (fp32) may be None."""
+    n = params.numel()
+    for name, t in (("grads", grads), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq),
+                    ("master", master)):
+        if t is not None and t.numel() != n:
+            raise MuonError(MUON_ERR_INVALID_ARG, f"{name} has {t.numel()} elements, expected {n}")
+    h = _ahp(hp)
+    _check(lib().adamw_step(_ptr(params), dtype_code(params.dtype), _ptr(master), _ptr(grads),
+                            dtype_code(grads.dtype), _ptr(exp_avg), _ptr(exp_avg_sq), n,
+                            ctypes.byref(h), int(step), _stream(stream)))

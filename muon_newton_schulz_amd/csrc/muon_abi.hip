@@ -1,0 +1,552 @@
+// Host side of the library: validation, planning (orientation, padding,
+// workspace layout, tile lists, waves) and the C ABI declared in muon.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "muon.h"
+#include "muon_internal.h"
+
+using muon::Item;
+using muon::MatDev;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return MUON_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct Wave {
+  int mat_begin = 0, mat_end = 0;
+  int64_t k1_begin = 0, k1_count = 0;      // into the k1 item table
+  int64_t syrk_begin = 0, syrk_count = 0;  // phases 1 and 2 share the list
+  int64_t bx_begin = 0, bx_count = 0;
+  size_t partial_off = 0, norm_off = 0, inv_off = 0;  // byte offsets in the workspace
+  size_t bytes = 0;
+};
+
+}  // namespace
+
+struct muon_plan {
+  int device = 0;
+  int32_t n_mats = 0;
+  int64_t flat_numel = 0;
+  int32_t param_dtype = 0, grad_dtype = 0, ns_dtype = 0;
+  int tile = 0;
+  size_t ws_bytes = 0;
+  std::vector<MatDev> mats;
+  std::vector<Item> k1_items, syrk_items, bx_items;
+  std::vector<Wave> waves;
+  // device copies
+  void* d_tables = nullptr;
+  MatDev* d_mats = nullptr;
+  Item* d_k1 = nullptr;
+  Item* d_syrk = nullptr;
+  Item* d_bx = nullptr;
+  double flops_per_iter = 0.0;
+};
+
+namespace {
+
+size_t ns_elem_bytes(int ns_dtype) { return ns_dtype == MUON_DTYPE_BF16 ? 2 : 4; }
+
+bool dtype_ok(int32_t d) { return d == MUON_DTYPE_FP32 || d == MUON_DTYPE_BF16; }
+
+// Per-matrix workspace elements (NS dtype): X, X^T x2, A, B.
+int64_t matrix_ws_elems(const MatDev& m) {
+  const int64_t mn = static_cast<int64_t>(m.m_pad) * m.n_pad;
+  const int64_t mm = static_cast<int64_t>(m.m_pad) * m.m_pad;
+  return 3 * mn + 2 * mm;
+}
+
+// Build every host-side table; no HIP call.
+int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
+               int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype, size_t workspace_cap,
+               muon_plan& p) {
+  if (n_mats < 0) return fail(MUON_ERR_INVALID_ARG, "n_mats < 0");
+  if (n_mats > 0 && mats == nullptr) return fail(MUON_ERR_INVALID_ARG, "mats is null");
+  if (flat_numel < 0) return fail(MUON_ERR_INVALID_ARG, "flat_numel < 0");
+  if (!dtype_ok(param_dtype) || !dtype_ok(grad_dtype) || !dtype_ok(ns_dtype))
+    return fail(MUON_ERR_BAD_DTYPE, "dtype must be MUON_DTYPE_FP32 or MUON_DTYPE_BF16");
+  p.n_mats = n_mats;
+  p.flat_numel = flat_numel;
+  p.param_dtype = param_dtype;
+  p.grad_dtype = grad_dtype;
+  p.ns_dtype = ns_dtype;
+  p.tile = ns_dtype == MUON_DTYPE_BF16 ? muon::kTileBf16 : muon::kTileFp32;
+  const int T = p.tile;
+
+  // shape checks
+  for (int32_t i = 0; i < n_mats; ++i) {
+    const muon_matrix_t& m = mats[i];
+    if (m.rows < 1 || m.cols < 1)
+      return fail(MUON_ERR_BAD_SHAPE, "matrix " + std::to_string(i) + ": rows and cols must be >= 1");
+    if (m.offset < 0)
+      return fail(MUON_ERR_BAD_SHAPE, "matrix " + std::to_string(i) + ": negative offset");
+    const int64_t numel = static_cast<int64_t>(m.rows) * m.cols;
+    if (m.offset > flat_numel || numel > flat_numel - m.offset)
+      return fail(MUON_ERR_BAD_SHAPE,
+                  "matrix " + std::to_string(i) + ": extends past the flat buffer");
+    // tile coordinates are packed in 16 bits
+    if (round_up(std::max(m.rows, m.cols), T) / muon::kEwTile > 0xffff)
+      return fail(MUON_ERR_BAD_SHAPE, "matrix " + std::to_string(i) + ": dimension too large");
+  }
+  // overlap check
+  {
+    std::vector<int32_t> order(n_mats);
+    for (int32_t i = 0; i < n_mats; ++i) order[i] = i;
+    std::sort(order.begin(), order.end(),
+              [&](int32_t a, int32_t b) { return mats[a].offset < mats[b].offset; });
+    for (int32_t k = 1; k < n_mats; ++k) {
+      const muon_matrix_t& a = mats[order[k - 1]];
+      const muon_matrix_t& b = mats[order[k]];
+      if (a.offset + static_cast<int64_t>(a.rows) * a.cols > b.offset)
+        return fail(MUON_ERR_OVERLAP, "matrices " + std::to_string(order[k - 1]) + " and " +
+                                          std::to_string(order[k]) + " overlap");
+    }
+  }
+
+  // orientation and padding
+  p.mats.resize(n_mats);
+  for (int32_t i = 0; i < n_mats; ++i) {
+    MatDev& d = p.mats[i];
+    std::memset(&d, 0, sizeof(d));
+    d.off = mats[i].offset;
+    d.rows = mats[i].rows;
+    d.cols = mats[i].cols;
+    d.trans = d.rows > d.cols ? 1 : 0;
+    d.m_pad = static_cast<int32_t>(round_up(std::min(d.rows, d.cols), T));
+    d.n_pad = static_cast<int32_t>(round_up(std::max(d.rows, d.cols), T));
+    const double m = std::min(d.rows, d.cols), n = std::max(d.rows, d.cols);
+    p.flops_per_iter += m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n;
+  }
+
+  // waves: consecutive matrices while the wave's workspace fits the cap
+  const size_t eb = ns_elem_bytes(ns_dtype);
+  auto k1_tiles_of = [&](const MatDev& d) {
+    const int64_t rp = d.trans ? d.n_pad : d.m_pad, cp = d.trans ? d.m_pad : d.n_pad;
+    return (rp / muon::kEwTile) * (cp / muon::kEwTile);
+  };
+  auto fixed_bytes = [&](int64_t k1, int64_t nm) {
+    // partial sums (one per k1 tile), norms and inverse norms (one per matrix)
+    return align_up(static_cast<size_t>(k1) * 4, kAlign) +
+           2 * align_up(static_cast<size_t>(nm) * 4, kAlign);
+  };
+  {
+    int32_t i = 0;
+    while (i < n_mats) {
+      Wave w;
+      w.mat_begin = i;
+      size_t mat_bytes = 0;
+      int64_t k1 = 0;
+      int32_t j = i;
+      while (j < n_mats) {
+        const size_t mb = align_up(static_cast<size_t>(matrix_ws_elems(p.mats[j])) * eb, kAlign);
+        const int64_t k1j = k1_tiles_of(p.mats[j]);
+        const size_t total = mat_bytes + mb + fixed_bytes(k1 + k1j, j - i + 1);
+        if (workspace_cap != 0 && total > workspace_cap) break;
+        mat_bytes += mb;
+        k1 += k1j;
+        ++j;
+      }
+      if (j == i)
+        return fail(MUON_ERR_WORKSPACE_TOO_SMALL,
+                    "matrix " + std::to_string(i) + " alone needs more workspace than the cap");
+      w.mat_end = j;
+      p.waves.push_back(w);
+      i = j;
+    }
+  }
+
+  // per-wave layout and tile lists
+  size_t ws_max = 0;
+  for (Wave& w : p.waves) {
+    const int nm = w.mat_end - w.mat_begin;
+    int64_t k1 = 0;
+    for (int m = w.mat_begin; m < w.mat_end; ++m) k1 += k1_tiles_of(p.mats[m]);
+    size_t off = 0;
+    w.partial_off = off;
+    off += align_up(static_cast<size_t>(k1) * 4, kAlign);
+    w.norm_off = off;
+    off += align_up(static_cast<size_t>(nm) * 4, kAlign);
+    w.inv_off = off;
+    off += align_up(static_cast<size_t>(nm) * 4, kAlign);
+    // matrices: offsets in NS elements from the workspace base
+    w.k1_begin = static_cast<int64_t>(p.k1_items.size());
+    for (int m = w.mat_begin; m < w.mat_end; ++m) {
+      MatDev& d = p.mats[m];
+      d.widx = m - w.mat_begin;
+      const int64_t mn = static_cast<int64_t>(d.m_pad) * d.n_pad;
+      const int64_t mm = static_cast<int64_t>(d.m_pad) * d.m_pad;
+      const int64_t base = static_cast<int64_t>(off / eb);
+      d.ws_x = base;
+      d.ws_xt[0] = base + mn;
+      d.ws_xt[1] = base + 2 * mn;
+      d.ws_a = base + 3 * mn;
+      d.ws_b = base + 3 * mn + mm;
+      off += align_up(static_cast<size_t>(matrix_ws_elems(d)) * eb, kAlign);
+      // elementwise tiles over the natural padded extent, row-major
+      const int64_t rp = d.trans ? d.n_pad : d.m_pad, cp = d.trans ? d.m_pad : d.n_pad;
+      d.k1_begin = static_cast<int32_t>(static_cast<int64_t>(p.k1_items.size()) - w.k1_begin);
+      d.k1_count = static_cast<int32_t>((rp / muon::kEwTile) * (cp / muon::kEwTile));
+      for (int64_t r = 0; r < rp / muon::kEwTile; ++r)
+        for (int64_t c = 0; c < cp / muon::kEwTile; ++c)
+          p.k1_items.push_back(Item{m, static_cast<int32_t>((r << 16) | c)});
+    }
+    w.k1_count = static_cast<int64_t>(p.k1_items.size()) - w.k1_begin;
+    w.bytes = off;
+    ws_max = std::max(ws_max, off);
+
+    // GEMM tile lists, most expensive (longest K) first; within equal cost
+    // keep matrix-major, row-major order so neighbours share operand panels.
+    struct Keyed { int64_t cost; Item it; };
+    std::vector<Keyed> syrk, bx;
+    for (int m = w.mat_begin; m < w.mat_end; ++m) {
+      const MatDev& d = p.mats[m];
+      const int mt = d.m_pad / T, nt = d.n_pad / T;
+      for (int a = 0; a < mt; ++a)
+        for (int b = a; b < mt; ++b)
+          syrk.push_back({d.n_pad, Item{m, (a << 16) | b}});
+      for (int a = 0; a < mt; ++a)
+        for (int b = 0; b < nt; ++b) bx.push_back({d.m_pad, Item{m, (a << 16) | b}});
+    }
+    auto by_cost = [](const Keyed& x, const Keyed& y) { return x.cost > y.cost; };
+    std::stable_sort(syrk.begin(), syrk.end(), by_cost);
+    std::stable_sort(bx.begin(), bx.end(), by_cost);
+    w.syrk_begin = static_cast<int64_t>(p.syrk_items.size());
+    w.syrk_count = static_cast<int64_t>(syrk.size());
+    for (auto& k : syrk) p.syrk_items.push_back(k.it);
+    w.bx_begin = static_cast<int64_t>(p.bx_items.size());
+    w.bx_count = static_cast<int64_t>(bx.size());
+    for (auto& k : bx) p.bx_items.push_back(k.it);
+    if (w.k1_count > 0x7fffffff || w.syrk_count > 0x7fffffff || w.bx_count > 0x7fffffff)
+      return fail(MUON_ERR_BAD_SHAPE, "too many tiles in one wave");
+  }
+  p.ws_bytes = ws_max;
+  return MUON_OK;
+}
+
+int upload_plan(muon_plan& p) {
+  hipError_t e = hipGetDevice(&p.device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  const size_t b_mats = align_up(p.mats.size() * sizeof(MatDev), kAlign);
+  const size_t b_k1 = align_up(p.k1_items.size() * sizeof(Item), kAlign);
+  const size_t b_syrk = align_up(p.syrk_items.size() * sizeof(Item), kAlign);
+  const size_t b_bx = align_up(p.bx_items.size() * sizeof(Item), kAlign);
+  const size_t total = b_mats + b_k1 + b_syrk + b_bx;
+  if (total == 0) return MUON_OK;
+  e = hipMalloc(&p.d_tables, total);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(plan tables)");
+  char* base = static_cast<char*>(p.d_tables);
+  p.d_mats = reinterpret_cast<MatDev*>(base);
+  p.d_k1 = reinterpret_cast<Item*>(base + b_mats);
+  p.d_syrk = reinterpret_cast<Item*>(base + b_mats + b_k1);
+  p.d_bx = reinterpret_cast<Item*>(base + b_mats + b_k1 + b_syrk);
+  std::vector<char> host(total, 0);
+  std::memcpy(host.data(), p.mats.data(), p.mats.size() * sizeof(MatDev));
+  std::memcpy(host.data() + b_mats, p.k1_items.data(), p.k1_items.size() * sizeof(Item));
+  std::memcpy(host.data() + b_mats + b_k1, p.syrk_items.data(), p.syrk_items.size() * sizeof(Item));
+  std::memcpy(host.data() + b_mats + b_k1 + b_syrk, p.bx_items.data(),
+              p.bx_items.size() * sizeof(Item));
+  e = hipMemcpy(p.d_tables, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(plan tables)");
+  return MUON_OK;
+}
+
+int check_step_common(const muon_plan_t* plan, int32_t wave, const void* workspace,
+                      size_t workspace_bytes) {
+  if (plan == nullptr) return fail(MUON_ERR_INVALID_ARG, "plan is null");
+  if (wave < 0 || wave >= static_cast<int32_t>(plan->waves.size()))
+    return fail(MUON_ERR_INVALID_ARG, "wave index out of range");
+  if (workspace == nullptr) return fail(MUON_ERR_INVALID_ARG, "workspace is null");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan->ws_bytes)
+    return fail(MUON_ERR_WORKSPACE_TOO_SMALL,
+                "workspace has " + std::to_string(workspace_bytes) + " bytes, plan needs " +
+                    std::to_string(plan->ws_bytes));
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(MUON_ERR_INVALID_ARG, "current device differs from the plan's device");
+  return MUON_OK;
+}
+
+int check_hparams(const muon_hparams_t* hp) {
+  if (hp == nullptr) return fail(MUON_ERR_INVALID_ARG, "hparams is null");
+  const float vals[] = {hp->lr, hp->weight_decay, hp->momentum, hp->ns_a, hp->ns_b,
+                        hp->ns_c, hp->eps, hp->rms_target};
+  for (float v : vals)
+    if (!std::isfinite(v)) return fail(MUON_ERR_INVALID_ARG, "non-finite hyperparameter");
+  if (hp->ns_steps < 0 || hp->ns_steps > 1000)
+    return fail(MUON_ERR_INVALID_ARG, "ns_steps must be in [0, 1000]");
+  if (hp->scale_mode < 0 || hp->scale_mode > 2)
+    return fail(MUON_ERR_INVALID_ARG, "scale_mode must be 0, 1 or 2");
+  if (hp->eps < 0.0f) return fail(MUON_ERR_INVALID_ARG, "eps must be >= 0");
+  return MUON_OK;
+}
+
+inline char* ws_bytes_ptr(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+muon::GemmArgs gemm_args(const muon_plan_t* p, const Wave& w, void* ws, const muon_hparams_t* hp,
+                         int iter, const Item* items) {
+  muon::GemmArgs g;
+  g.mats = p->d_mats;
+  g.items = items;
+  g.ws = ws;
+  g.inv = reinterpret_cast<const float*>(ws_bytes_ptr(ws, w.inv_off));
+  g.a = hp->ns_a;
+  g.b = hp->ns_b;
+  g.c = hp->ns_c;
+  g.first = iter == 0;
+  g.last = iter == hp->ns_steps - 1;
+  g.xt_cur = iter & 1;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* muon_status_string(int32_t status) {
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_INVALID_ARG: return "invalid argument";
+    case MUON_ERR_BAD_SHAPE: return "bad shape";
+    case MUON_ERR_OVERLAP: return "matrices overlap";
+    case MUON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MUON_ERR_BAD_DTYPE: return "bad dtype";
+    case MUON_ERR_HIP: return "HIP runtime error";
+    case MUON_ERR_UNSUPPORTED: return "unsupported";
+    default: return "unknown status";
+  }
+}
+
+const char* muon_last_error(void) { return g_last_error.c_str(); }
+
+int muon_workspace_size(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
+                        int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
+                        size_t workspace_cap, size_t* workspace_bytes) {
+  if (workspace_bytes == nullptr) return fail(MUON_ERR_INVALID_ARG, "workspace_bytes is null");
+  muon_plan p;
+  const int rc = build_plan(mats, n_mats, flat_numel, param_dtype, grad_dtype, ns_dtype,
+                            workspace_cap, p);
+  if (rc != MUON_OK) return rc;
+  *workspace_bytes = p.ws_bytes;
+  return MUON_OK;
+}
+
+int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
+                     int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
+                     size_t workspace_cap, muon_plan_t** out, size_t* workspace_bytes) {
+  if (out == nullptr) return fail(MUON_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  muon_plan* p = new (std::nothrow) muon_plan();
+  if (p == nullptr) return fail(MUON_ERR_INVALID_ARG, "out of host memory");
+  int rc = build_plan(mats, n_mats, flat_numel, param_dtype, grad_dtype, ns_dtype,
+                      workspace_cap, *p);
+  if (rc == MUON_OK) rc = upload_plan(*p);
+  if (rc != MUON_OK) {
+    muon_plan_destroy(p);
+    return rc;
+  }
+  if (workspace_bytes) *workspace_bytes = p->ws_bytes;
+  *out = p;
+  return MUON_OK;
+}
+
+void muon_plan_destroy(muon_plan_t* plan) {
+  if (plan == nullptr) return;
+  if (plan->d_tables) {
+    int cur = -1;
+    if (hipGetDevice(&cur) == hipSuccess && cur != plan->device) {
+      (void)hipSetDevice(plan->device);
+      (void)hipFree(plan->d_tables);
+      (void)hipSetDevice(cur);
+    } else {
+      (void)hipFree(plan->d_tables);
+    }
+  }
+  delete plan;
+}
+
+int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {
+  if (plan == nullptr || info == nullptr) return fail(MUON_ERR_INVALID_ARG, "null argument");
+  info->n_mats = plan->n_mats;
+  info->n_waves = static_cast<int32_t>(plan->waves.size());
+  info->tile = plan->tile;
+  info->ns_dtype = plan->ns_dtype;
+  info->k1_tiles = static_cast<int64_t>(plan->k1_items.size());
+  info->syrk_tiles = static_cast<int64_t>(plan->syrk_items.size());
+  info->bx_tiles = static_cast<int64_t>(plan->bx_items.size());
+  info->workspace_bytes = plan->ws_bytes;
+  info->ns_flops_per_iter_alg = plan->flops_per_iter;
+  return MUON_OK;
+}
+
+int muon_stage_momentum(const muon_plan_t* plan, int32_t wave, const void* grads,
+                        float* momentum, void* workspace, size_t workspace_bytes,
+                        const muon_hparams_t* hp, hipStream_t stream) {
+  int rc = check_step_common(plan, wave, workspace, workspace_bytes);
+  if (rc != MUON_OK) return rc;
+  if ((rc = check_hparams(hp)) != MUON_OK) return rc;
+  if (grads == nullptr || momentum == nullptr)
+    return fail(MUON_ERR_INVALID_ARG, "grads or momentum is null");
+  const Wave& w = plan->waves[wave];
+  float* partials = reinterpret_cast<float*>(ws_bytes_ptr(workspace, w.partial_off));
+  hipError_t e = muon::launch_momentum(plan->d_mats, plan->d_k1 + w.k1_begin,
+                                       static_cast<int>(w.k1_count), plan->grad_dtype,
+                                       plan->ns_dtype, grads, momentum, workspace, partials,
+                                       hp->momentum, hp->nesterov, stream);
+  if (e != hipSuccess) return hip_fail(e, "momentum kernel launch");
+  e = muon::launch_norm_finalize(plan->d_mats, w.mat_begin, w.mat_end - w.mat_begin, partials,
+                                 reinterpret_cast<float*>(ws_bytes_ptr(workspace, w.norm_off)),
+                                 reinterpret_cast<float*>(ws_bytes_ptr(workspace, w.inv_off)),
+                                 hp->eps, stream);
+  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
+  return MUON_OK;
+}
+
+int muon_stage_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
+                        size_t workspace_bytes, const muon_hparams_t* hp, int32_t iter,
+                        int32_t phase, hipStream_t stream) {
+  int rc = check_step_common(plan, wave, workspace, workspace_bytes);
+  if (rc != MUON_OK) return rc;
+  if ((rc = check_hparams(hp)) != MUON_OK) return rc;
+  if (iter < 0 || iter >= hp->ns_steps) return fail(MUON_ERR_INVALID_ARG, "iter out of range");
+  if (phase < 1 || phase > 3) return fail(MUON_ERR_INVALID_ARG, "phase must be 1, 2 or 3");
+  if (phase == 2 && hp->ns_c == 0.0f)
+    return fail(MUON_ERR_INVALID_ARG, "phase 2 is skipped when ns_c == 0");
+  const Wave& w = plan->waves[wave];
+  const Item* items = phase == 3 ? plan->d_bx + w.bx_begin : plan->d_syrk + w.syrk_begin;
+  const int n = static_cast<int>(phase == 3 ? w.bx_count : w.syrk_count);
+  const muon::GemmArgs g = gemm_args(plan, w, workspace, hp, iter, items);
+  const hipError_t e = muon::launch_ns_phase(plan->ns_dtype, phase, n, g, stream);
+  if (e != hipSuccess) return hip_fail(e, "NS kernel launch");
+  return MUON_OK;
+}
+
+int muon_stage_apply(const muon_plan_t* plan, int32_t wave, void* params, void* workspace,
+                     size_t workspace_bytes, const muon_hparams_t* hp, float* out_update,
+                     hipStream_t stream) {
+  int rc = check_step_common(plan, wave, workspace, workspace_bytes);
+  if (rc != MUON_OK) return rc;
+  if ((rc = check_hparams(hp)) != MUON_OK) return rc;
+  if (params == nullptr) return fail(MUON_ERR_INVALID_ARG, "params is null");
+  const Wave& w = plan->waves[wave];
+  const hipError_t e = muon::launch_apply(
+      plan->d_mats, plan->d_k1 + w.k1_begin, static_cast<int>(w.k1_count), plan->param_dtype,
+      plan->ns_dtype, params, workspace,
+      reinterpret_cast<const float*>(ws_bytes_ptr(workspace, w.inv_off)),
+      hp->ns_steps == 0 ? 1.0f : 0.0f, hp->ns_steps & 1, hp->lr, hp->weight_decay,
+      hp->scale_mode, hp->rms_target, out_update, stream);
+  if (e != hipSuccess) return hip_fail(e, "apply kernel launch");
+  return MUON_OK;
+}
+
+int muon_stage_export_x(const muon_plan_t* plan, int32_t wave, const void* workspace,
+                        size_t workspace_bytes, int32_t iter_done, float* out,
+                        hipStream_t stream) {
+  int rc = check_step_common(plan, wave, workspace, workspace_bytes);
+  if (rc != MUON_OK) return rc;
+  if (out == nullptr) return fail(MUON_ERR_INVALID_ARG, "out is null");
+  if (iter_done < 0) return fail(MUON_ERR_INVALID_ARG, "iter_done < 0");
+  const Wave& w = plan->waves[wave];
+  const hipError_t e =
+      muon::launch_export(plan->d_mats, plan->d_k1 + w.k1_begin, static_cast<int>(w.k1_count),
+                          plan->ns_dtype, workspace, iter_done & 1, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "export kernel launch");
+  return MUON_OK;
+}
+
+int muon_stage_export_norms(const muon_plan_t* plan, int32_t wave, const void* workspace,
+                            size_t workspace_bytes, float* out, hipStream_t stream) {
+  int rc = check_step_common(plan, wave, workspace, workspace_bytes);
+  if (rc != MUON_OK) return rc;
+  if (out == nullptr) return fail(MUON_ERR_INVALID_ARG, "out is null");
+  const Wave& w = plan->waves[wave];
+  const hipError_t e = hipMemcpyAsync(
+      out, static_cast<const char*>(workspace) + w.norm_off,
+      static_cast<size_t>(w.mat_end - w.mat_begin) * sizeof(float), hipMemcpyDeviceToDevice,
+      stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(norms)");
+  return MUON_OK;
+}
+
+int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* momentum,
+              void* workspace, size_t workspace_bytes, const muon_hparams_t* hp,
+              float* out_update, hipStream_t stream) {
+  if (plan == nullptr) return fail(MUON_ERR_INVALID_ARG, "plan is null");
+  int rc = check_hparams(hp);
+  if (rc != MUON_OK) return rc;
+  if (plan->waves.empty()) return MUON_OK;
+  if (params == nullptr || grads == nullptr || momentum == nullptr)
+    return fail(MUON_ERR_INVALID_ARG, "params, grads or momentum is null");
+  for (int32_t w = 0; w < static_cast<int32_t>(plan->waves.size()); ++w) {
+    rc = muon_stage_momentum(plan, w, grads, momentum, workspace, workspace_bytes, hp, stream);
+    if (rc != MUON_OK) return rc;
+    for (int32_t it = 0; it < hp->ns_steps; ++it) {
+      rc = muon_stage_ns_phase(plan, w, workspace, workspace_bytes, hp, it, 1, stream);
+      if (rc == MUON_OK && hp->ns_c != 0.0f)
+        rc = muon_stage_ns_phase(plan, w, workspace, workspace_bytes, hp, it, 2, stream);
+      if (rc == MUON_OK)
+        rc = muon_stage_ns_phase(plan, w, workspace, workspace_bytes, hp, it, 3, stream);
+      if (rc != MUON_OK) return rc;
+    }
+    rc = muon_stage_apply(plan, w, params, workspace, workspace_bytes, hp, out_update, stream);
+    if (rc != MUON_OK) return rc;
+  }
+  return MUON_OK;
+}
+
+int adamw_step(void* params, int32_t param_dtype, float* master, const void* grads,
+               int32_t grad_dtype, float* exp_avg, float* exp_avg_sq, int64_t n,
+               const adamw_hparams_t* hp, int64_t step, hipStream_t stream) {
+  if (hp == nullptr) return fail(MUON_ERR_INVALID_ARG, "hparams is null");
+  if (!dtype_ok(param_dtype) || !dtype_ok(grad_dtype))
+    return fail(MUON_ERR_BAD_DTYPE, "dtype must be MUON_DTYPE_FP32 or MUON_DTYPE_BF16");
+  if (param_dtype == MUON_DTYPE_BF16 && master == nullptr)
+    return fail(MUON_ERR_INVALID_ARG, "bf16 parameters need a fp32 master copy");
+  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n < 0");
+  if (step < 1) return fail(MUON_ERR_INVALID_ARG, "step must be >= 1 (t starts at 1)");
+  const float vals[] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+  for (float v : vals)
+    if (!std::isfinite(v)) return fail(MUON_ERR_INVALID_ARG, "non-finite hyperparameter");
+  if (hp->beta1 < 0.0f || hp->beta1 >= 1.0f || hp->beta2 < 0.0f || hp->beta2 >= 1.0f)
+    return fail(MUON_ERR_INVALID_ARG, "betas must be in [0, 1)");
+  if (n == 0) return MUON_OK;
+  if (params == nullptr || grads == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr)
+    return fail(MUON_ERR_INVALID_ARG, "null buffer");
+  // bias corrections in fp64 on the host
+  const double bc1 = 1.0 - std::pow(static_cast<double>(hp->beta1), static_cast<double>(step));
+  const double bc2 = 1.0 - std::pow(static_cast<double>(hp->beta2), static_cast<double>(step));
+  const float lr_bc1 = static_cast<float>(static_cast<double>(hp->lr) / bc1);
+  const float rsqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+  const hipError_t e =
+      muon::launch_adamw(params, param_dtype, master, grads, grad_dtype, exp_avg, exp_avg_sq, n,
+                         hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, lr_bc1,
+                         rsqrt_bc2, stream);
+  if (e != hipSuccess) return hip_fail(e, "AdamW kernel launch");
+  return MUON_OK;
+}
+
+}  // extern "C"

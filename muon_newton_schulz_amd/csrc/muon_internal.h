@@ -1,0 +1,86 @@
+// Internal types shared by the host planner and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+// Edge of the elementwise tiles used by the momentum and apply kernels.
+constexpr int kEwTile = 64;
+// GEMM tile edges: bf16 MFMA engine and fp32 engine.
+constexpr int kTileBf16 = 256;
+constexpr int kTileFp32 = 64;
+
+// One matrix of a plan, as the device sees it.  "Oriented" dims put the
+// short side first (m = min(rows, cols), n = max(rows, cols)); tall
+// matrices (rows > cols) are iterated transposed.  The natural layout
+// buffer holds the matrix as the caller stores it ([rows, cols], padded),
+// the transposed buffer holds its transpose.
+struct MatDev {
+  int64_t off;      // element offset in the flat params/grads/momentum
+  int32_t rows, cols;
+  int32_t m_pad, n_pad;  // oriented, padded to the GEMM tile
+  int32_t trans;         // 1 if rows > cols
+  int32_t widx;          // index of the matrix within its wave
+  int32_t k1_begin;      // first elementwise tile of this matrix (wave-local)
+  int32_t k1_count;      // number of elementwise tiles of this matrix
+  // element offsets (in NS elements) into the workspace
+  int64_t ws_x;          // X  : m_pad x n_pad, row-major (oriented iterate)
+  int64_t ws_xt[2];      // X^T: n_pad x m_pad, ping-pong
+  int64_t ws_a;          // A  : m_pad x m_pad
+  int64_t ws_b;          // B  : m_pad x m_pad
+};
+
+// A tile work item: matrix index (plan-global) and packed tile coords.
+struct Item {
+  int32_t mat;
+  int32_t rc;  // (row_tile << 16) | col_tile
+};
+
+struct GemmArgs {
+  const MatDev* mats;
+  const Item* items;
+  void* ws;           // workspace base (NS element type)
+  const float* inv;   // wave-local 1/(||U||_F + eps)
+  float a, b, c;
+  int32_t first;      // first NS iteration: fold the normalisation in
+  int32_t last;       // last NS iteration: only the natural layout is needed
+  int32_t xt_cur;     // X^T buffer read by phase 3 (written: 1 - xt_cur)
+};
+
+// kernel launchers (defined in the .hip files)
+hipError_t launch_momentum(const MatDev* mats, const Item* items, int n_items,
+                           int grad_dtype, int ns_dtype, const void* grads, float* mom,
+                           void* ws, float* partials, float mu, int nesterov,
+                           hipStream_t s);
+hipError_t launch_norm_finalize(const MatDev* mats, int mat_begin, int n_mats,
+                                const float* partials, float* norms, float* inv,
+                                float eps, hipStream_t s);
+hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int param_dtype,
+                        int ns_dtype, void* params, const void* ws, const float* inv,
+                        float o_scale_by_inv, int xt_final, float lr, float wd,
+                        int scale_mode, float rms_target, float* out_update,
+                        hipStream_t s);
+hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int ns_dtype,
+                         const void* ws, int xt_idx, float* out, hipStream_t s);
+hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, const GemmArgs& args,
+                           hipStream_t s);
+hipError_t launch_adamw(void* params, int param_dtype, float* master, const void* grads,
+                        int grad_dtype, float* m, float* v, int64_t n, float lr,
+                        float beta1, float beta2, float eps, float wd, float lr_bc1,
+                        float rsqrt_bc2, hipStream_t s);
+
+// bf16 <-> fp32 (bf16 stored as its 16-bit pattern)
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// round-to-nearest-even; NaN stays a (quiet) NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+}  // namespace muon

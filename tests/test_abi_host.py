@@ -1,0 +1,99 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol
+include/muon.h declares, and rejects bad input before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import muon_newton_schulz_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "muon.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_binding_names():
+    assert set(_declared_functions()) == set(M.EXPORTED)
+
+
+def test_library_loads_and_exports_every_symbol():
+    L = M.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert M.muon_status_string(0) == "ok"
+    for code in range(-7, 0):
+        assert M.muon_status_string(code) not in ("ok", "unknown status")
+    assert M.muon_status_string(-99) == "unknown status"
+
+
+def _err(fn, *a, **k):
+    with pytest.raises(M.MuonError) as e:
+        fn(*a, **k)
+    return e.value.status
+
+
+def test_workspace_size_validation():
+    ws = M.muon_workspace_size
+    assert _err(ws, [(0, 0, 5)], 10, "bf16", "bf16", "bf16") == M.MUON_ERR_BAD_SHAPE
+    assert _err(ws, [(0, 4, 4)], 15, "bf16", "bf16", "bf16") == M.MUON_ERR_BAD_SHAPE
+    assert _err(ws, [(-1, 2, 2)], 15, "bf16", "bf16", "bf16") == M.MUON_ERR_BAD_SHAPE
+    assert _err(ws, [(0, 4, 4), (15, 2, 2)], 100, "bf16", "bf16", "bf16") == M.MUON_ERR_OVERLAP
+    assert _err(ws, [(20, 4, 4), (0, 5, 5)], 100, "bf16", "bf16", "bf16") == M.MUON_ERR_OVERLAP
+    with pytest.raises(M.MuonError):
+        ws([(0, 4, 4)], 16, "fp16", "bf16", "bf16")
+    # a cap smaller than one matrix needs
+    assert _err(ws, [(0, 300, 300)], 90000, "bf16", "bf16", "bf16", 1024) == \
+        M.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert "matrix 0" in M.muon_last_error()
+
+
+def test_workspace_size_layout():
+    # bf16 NS pads to 256: a 300x100 (tall) matrix is oriented 100x300 ->
+    # m_pad 256, n_pad 512; X, X^T x2 (3*256*512) and A, B (2*256*256), bf16.
+    b = M.muon_workspace_size([(0, 300, 100)], 30000, "bf16", "bf16", "bf16")
+    k1 = (512 // 64) * (256 // 64)
+    fixed = 256 + 256 + 256  # partials (k1*4 <= 256), norms, inverse norms
+    assert k1 * 4 <= 256
+    assert b == fixed + 2 * (3 * 256 * 512 + 2 * 256 * 256)
+    # fp32 NS pads to 64: 128x256 -> X, X^T x2 and A, B in fp32
+    b = M.muon_workspace_size([(0, 128, 256)], 128 * 256, "fp32", "fp32", "fp32")
+    k1 = 2 * 4
+    assert b == 256 * 3 + 4 * (3 * 128 * 256 + 2 * 128 * 128)
+    # empty plan
+    assert M.muon_workspace_size([], 0, "bf16", "bf16", "bf16") == 0
+
+
+def test_waves_bound_the_workspace():
+    mats = [(k * 512 * 512, 512, 512) for k in range(6)]
+    one = M.muon_workspace_size(mats[:1], 512 * 512, "bf16", "bf16", "bf16")
+    full = M.muon_workspace_size(mats, 6 * 512 * 512, "bf16", "bf16", "bf16")
+    capped = M.muon_workspace_size(mats, 6 * 512 * 512, "bf16", "bf16", "bf16", 2 * one + 1024)
+    assert capped <= 2 * one + 1024
+    assert capped < full
+
+
+def test_adamw_validation_before_any_hip_call():
+    import torch
+    p = torch.zeros(8, dtype=torch.bfloat16)
+    g = torch.zeros(8, dtype=torch.bfloat16)
+    m = torch.zeros(8)
+    v = torch.zeros(8)
+    hp = M.AdamWHParamsC(0.01, 0.9, 0.95, 1e-8, 0.1)
+    assert _err(M.adamw_step, p, None, g, m, v, hp, 1, stream=0) == M.MUON_ERR_INVALID_ARG
+    p32 = torch.zeros(8)
+    assert _err(M.adamw_step, p32, None, p32, m, v, hp, 0, stream=0) == M.MUON_ERR_INVALID_ARG
+    bad = M.AdamWHParamsC(0.01, 1.0, 0.95, 1e-8, 0.1)
+    assert _err(M.adamw_step, p32, None, p32, m, v, bad, 1, stream=0) == M.MUON_ERR_INVALID_ARG
+    assert _err(M.adamw_step, p32, None, p32, m, torch.zeros(7), hp, 1, stream=0) == \
+        M.MUON_ERR_INVALID_ARG
