@@ -1,0 +1,275 @@
+"""Benchmark of one full optimizer step (Muon on every hidden matrix + AdamW
+on embedding, LM head and norm vectors) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--coef quintic|cubic]
+
+Prints ONE JSON line.  The step is launched through the C ABI stage entry
+points (the same launches muon_step makes, in the same order, on torch's
+current stream) so that HIP events can bracket each kernel inside the
+timed region.  Inputs are seeded synthetic tensors already resident in
+HBM; gradients stay fixed across steps (the optimizer work does not
+depend on their values).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense_d2048_l16")
+    ap.add_argument("--coef", default="quintic", choices=["quintic", "cubic"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also launch one plain device copy of this many MiB (counter scale)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, hp, sample_mats, adam_n):
+    """The fp64 oracle on a bounded sample of the same workload, timed on
+    the host cores.  Reported as NS TFLOP/s of the sample (same unit as
+    the GPU value) together with the wall time."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from muon_newton_schulz_amd import workloads as W
+    from oracle import muon_oracle as O
+
+    ohp = O.MuonHP(lr=hp.lr, weight_decay=hp.weight_decay, momentum=hp.momentum,
+                   nesterov=hp.nesterov, ns_a=hp.ns_a, ns_b=hp.ns_b, ns_c=hp.ns_c,
+                   ns_steps=hp.ns_steps, eps=hp.eps, scale_mode=hp.scale_mode,
+                   rms_target=hp.rms_target)
+    mats = wl.mats()
+    inputs = []
+    for i in sample_mats:
+        o, r, c = mats[i]
+        w = W.normal_tensor(r * c, wl.w_std, wl.param_dtype, W.seed_key(wl.config_id, 0, i, 0))
+        g = W.normal_tensor(r * c, wl.g_std, wl.grad_dtype, W.seed_key(wl.config_id, 1, i, 1))
+        inputs.append((w.double().numpy().reshape(r, c), g.double().numpy().reshape(r, c),
+                       np.zeros((r, c))))
+    grp = wl.adam[0]
+    ap = W.normal_tensor(adam_n, grp.p_std, "fp32", 99).double().numpy()
+    ag = W.normal_tensor(adam_n, grp.g_std, grp.grad_dtype, 98).double().numpy()
+    ahp = O.AdamWHP(wl.adam_hp.lr, wl.adam_hp.beta1, wl.adam_hp.beta2, wl.adam_hp.eps,
+                    wl.adam_hp.weight_decay)
+    t0 = time.perf_counter()
+    for (w, g, m) in inputs:
+        O.muon_matrix_math(w, g, m, ohp)
+    t1 = time.perf_counter()
+    O.adamw_step_stored(O.bf16_round(ap), ap, ag, np.zeros(adam_n), np.zeros(adam_n), ahp, 1,
+                        "bf16")
+    t2 = time.perf_counter()
+    flops = sum(W.ns_flops_matrix(mats[i][1], mats[i][2], hp.ns_steps, hp.ns_c)
+                for i in sample_mats)
+    threads = max((d.get("num_threads", 1) for d in threadpool_info()
+                   if d.get("user_api") == "blas"), default=1)
+    sample_params = sum(mats[i][1] * mats[i][2] for i in sample_mats)
+    return {
+        "value": flops / (t1 - t0) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle: full Muon step on {len(sample_mats)} of "
+                   f"{len(mats)} matrices ({sample_params / wl.muon_numel():.1%} of the Muon "
+                   f"params, {flops / 1e12:.2f} TFLOP of NS) in {t1 - t0:.1f} s, plus AdamW on "
+                   f"{adam_n} elements in {t2 - t1:.2f} s "
+                   f"({adam_n * 28 / (t2 - t1) / 1e9:.2f} GB/s algorithmic)"),
+        "muon_seconds": t1 - t0,
+        "adamw_seconds": t2 - t1,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(the path shards by whole matrices across GPUs, not implemented)"}))
+        sys.exit(2)
+
+    import torch
+
+    import muon_newton_schulz_amd as M
+    from muon_newton_schulz_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M.lib()
+    wl = W.workload(args.workload)
+    coef = W.QUINTIC if args.coef == "quintic" else W.CUBIC
+    hp = wl.muon_hp
+    hp.ns_a, hp.ns_b, hp.ns_c = coef
+    ahp = wl.adam_hp
+
+    # ---- inputs resident in HBM (seeded, generated on the device)
+    inp = W.make_muon_inputs(wl, dev, step=1)
+    plan = M.muon_plan_create(wl.mats(), wl.muon_numel(), wl.param_dtype, wl.grad_dtype, "bf16")
+    info = plan.info()
+    ws = plan.alloc_workspace(dev)
+    adam = [W.make_adam_inputs(wl, gi, device=dev, step=1) for gi in range(len(wl.adam))]
+    calib = None
+    if args.copy_calibration:
+        nb = args.copy_calibration << 20
+        calib = (torch.empty(nb, dtype=torch.uint8, device=dev),
+                 torch.empty(nb, dtype=torch.uint8, device=dev))
+        calib[0].fill_(1)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    n_waves = info.n_waves
+    phases = (1, 2, 3) if hp.ns_c != 0.0 else (1, 3)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    t_step = [0]
+
+    def one_step(record):
+        """One optimizer step; with ``record`` returns per-kernel event pairs."""
+        marks = {"momentum": [], "ns1": [], "ns2": [], "ns3": [], "apply": [], "adamw": []}
+
+        def timed(key, fn):
+            if record:
+                a, b = ev(), ev()
+                a.record(stream)
+                fn()
+                b.record(stream)
+                marks[key].append((a, b))
+            else:
+                fn()
+
+        for w in range(n_waves):
+            timed("momentum", lambda: M.muon_stage_momentum(plan, w, inp.grads, inp.momentum,
+                                                            ws, hp))
+            for it in range(hp.ns_steps):
+                for ph in phases:
+                    timed(f"ns{ph}", lambda: M.muon_stage_ns_phase(plan, w, ws, hp, it, ph))
+            timed("apply", lambda: M.muon_stage_apply(plan, w, inp.params, ws, hp))
+        t_step[0] += 1
+        for a in adam:
+            timed("adamw", lambda: M.adamw_step(a.param, a.master, a.grad, a.exp_avg,
+                                                a.exp_avg_sq, ahp, t_step[0]))
+        return marks
+
+    for _ in range(args.warmup):
+        one_step(False)
+    if calib is not None:
+        calib[1].copy_(calib[0])
+    torch.cuda.synchronize()
+
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    all_marks = []
+    for _ in range(args.steps):
+        all_marks.append(one_step(True))
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+
+    def avg_ms(key):
+        vals = [a.elapsed_time(b) for mk in all_marks for (a, b) in mk[key]]
+        return (sum(vals) / len(vals)) if vals else 0.0, len(vals) // max(1, args.steps)
+
+    k = {key: avg_ms(key) for key in ("momentum", "ns1", "ns2", "ns3", "apply", "adamw")}
+
+    # ---- algorithmic work
+    shapes = wl.shapes
+    mm = [(min(r, c), max(r, c)) for r, c in shapes]
+    f1 = sum(m * (m + 1) * n for m, n in mm)           # X X^T, one triangle
+    f2 = sum(m * m * (m + 1) for m, n in mm) if hp.ns_c != 0.0 else 0
+    f3 = sum(2 * m * m * n for m, n in mm)             # B X
+    ns_flops_step = (f1 + f2 + f3) * hp.ns_steps
+    ns_ms_step = sum(k[f"ns{p}"][0] * k[f"ns{p}"][1] for p in phases)
+    n_muon = wl.muon_numel()
+    mom_bytes = n_muon * W.momentum_bytes_per_param(wl.grad_dtype)
+    app_bytes = n_muon * W.apply_bytes_per_param(wl.param_dtype)
+    adam_bytes = [g.numel * W.adamw_bytes_per_param(g.param_dtype, g.grad_dtype, g.master)
+                  for g in wl.adam]
+    adam_ms_total = k["adamw"][0] * k["adamw"][1]
+
+    f3_tflops = f3 / (k["ns3"][0] * 1e-3) / 1e12
+    result = {
+        "metric": "Muon NS TFLOP/s (% MFMA peak) + AdamW/momentum HBM GB/s, 1 GPU",
+        "value": ns_flops_step / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, std^2) weights and gradients, generated on the device)",
+        "config": {
+            "workload": args.workload,
+            "muon_matrices": len(shapes),
+            "muon_params": n_muon,
+            "adamw_params": wl.adam_numel(),
+            "ns_steps": hp.ns_steps,
+            "ns_coefficients": list(coef),
+            "ns_dtype": "bf16",
+            "param_dtype": wl.param_dtype,
+            "waves": n_waves,
+            "workspace_GiB": round(plan.workspace_bytes / 2 ** 30, 3),
+        },
+        "value_definition": "algorithmic NS flops of one step / whole optimizer step time",
+        "roofline": {
+            "kernel": "k_ns_bf16<3> (X <- a X + B X)",
+            "bound": "mfma",
+            "achieved": f3_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": f3_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "flops_per_launch": f3,
+            "avg_launch_ms": k["ns3"][0],
+        },
+        "breakdown_ms_per_step": {
+            "momentum+norm": k["momentum"][0] * k["momentum"][1],
+            "ns_phase1_xxt": k["ns1"][0] * k["ns1"][1],
+            "ns_phase2_aa": k["ns2"][0] * k["ns2"][1],
+            "ns_phase3_bx": k["ns3"][0] * k["ns3"][1],
+            "apply": k["apply"][0] * k["apply"][1],
+            "adamw": adam_ms_total,
+        },
+        "ns_tflops_kernels_only": ns_flops_step / (ns_ms_step * 1e-3) / 1e12,
+        "ns_frac_of_peak": ns_flops_step / (ns_ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "phase_tflops": {
+            "xxt": f1 / (k["ns1"][0] * 1e-3) / 1e12,
+            "aa": (f2 / (k["ns2"][0] * 1e-3) / 1e12) if f2 else None,
+            "bx": f3_tflops,
+        },
+        "hbm_gbps": {
+            "momentum+norm": mom_bytes / (k["momentum"][0] * 1e-3) / 1e9,
+            "apply": app_bytes / (k["apply"][0] * 1e-3) / 1e9,
+            "adamw": sum(adam_bytes) / (adam_ms_total * 1e-3) / 1e9 if adam_ms_total else None,
+            "peak": PEAK_HBM_GBPS,
+        },
+        "wall_s_timed_region": wall1 - wall0,
+    }
+    if not args.no_cpu_baseline:
+        # first layer of the stack: 4 square + 3 rectangular matrices
+        sample = list(range(7)) if len(shapes) >= 7 else list(range(len(shapes)))
+        result["cpu_baseline"] = cpu_baseline(wl, hp, sample, 1 << 22)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
