@@ -2,8 +2,9 @@
 //
 //  k_momentum       momentum EMA (optimizer tutorial, section 2.1) and the
 //                   Nesterov look-ahead U, written into the NS workspace in
-//                   both the natural and the transposed layout, plus one
-//                   fixed-order partial sum of U^2 per 64x64 tile.
+//                   the oriented layout (tall matrices transposed through
+//                   an LDS tile), plus one fixed-order partial sum of U^2
+//                   per 64x64 tile.
 //  k_norm_finalize  per-matrix ||U||_F and 1/(||U||_F + eps) (Zhihu answer
 //                   on K2, section 4: the Frobenius norm bounds the
 //                   spectral norm).
@@ -21,6 +22,8 @@
 
 namespace muon {
 namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -42,22 +45,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Natural-layout padded dims and buffers of a matrix in the workspace.
-struct NatView {
-  int64_t nat, tra;  // element offsets of natural / transposed buffers
-  int rp, cp;        // natural padded rows / cols
+// Natural padded dims of a matrix: the oriented iterate is [m_pad][n_pad];
+// for a tall matrix that is the transpose of the natural [rows][cols].
+struct NatDims {
+  int rp, cp;  // natural padded rows / cols
 };
-__device__ __forceinline__ NatView nat_view(const MatDev& md, int xt_idx) {
-  NatView v;
-  v.rp = md.trans ? md.n_pad : md.m_pad;
-  v.cp = md.trans ? md.m_pad : md.n_pad;
-  v.nat = md.trans ? md.ws_xt[xt_idx] : md.ws_x;
-  v.tra = md.trans ? md.ws_x : md.ws_xt[xt_idx];
-  return v;
+__device__ __forceinline__ NatDims nat_dims(const MatDev& md) {
+  NatDims d;
+  d.rp = md.trans ? md.n_pad : md.m_pad;
+  d.cp = md.trans ? md.m_pad : md.n_pad;
+  return d;
 }
 
-// One 64x64 tile of one matrix per block, covering the padded extent so
-// the zero padding of the NS operands is (re)written every step.
+// One 64x64 tile (natural coordinates) of one matrix per block, covering
+// the padded extent so the zero padding of the NS operand is (re)written
+// every step.
 template <typename GT, typename UT>
 __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mats,
                                                   const Item* __restrict__ items,
@@ -70,9 +72,8 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
   const Item it = items[blockIdx.x];
   const MatDev md = mats[it.mat];
   const int r0 = (it.rc >> 16) * kEwTile, c0 = (it.rc & 0xffff) * kEwTile;
-  const NatView nv = nat_view(md, 0);
-  UT* nat = ws + nv.nat;
-  UT* tra = ws + nv.tra;
+  const NatDims nd = nat_dims(md);
+  UT* X = ws + md.ws_x[0];
   const int lc = threadIdx.x & 63, lr = threadIdx.x >> 6;
   const float omm = 1.0f - mu;
   const int c = c0 + lc;
@@ -89,19 +90,50 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
       u = nesterov ? mu * m + omm * g : m;
     }
     ss = fmaf(u, u, ss);
-    tile[rr][lc] = u;
-    Elem<UT>::st(nat, static_cast<int64_t>(r) * nv.cp + c, u);
+    if (md.trans) tile[rr][lc] = u;
+    else Elem<UT>::st(X, static_cast<int64_t>(r) * nd.cp + c, u);
   }
-  __syncthreads();
+  if (md.trans) {
+    // X = U^T: X[c][r], coalesced along r
+    __syncthreads();
 #pragma unroll 4
-  for (int q = 0; q < 16; ++q) {
-    const int cc = lr + 4 * q;
-    Elem<UT>::st(tra, static_cast<int64_t>(c0 + cc) * nv.rp + r0 + lc, tile[lc][cc]);
+    for (int q = 0; q < 16; ++q) {
+      const int cc = lr + 4 * q;
+      Elem<UT>::st(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + lc, tile[lc][cc]);
+    }
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
   __syncthreads();
   if (threadIdx.x == 0) partials[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+}
+
+// Reads the 64x64 natural-coordinate tile (r0, c0) of the oriented iterate
+// X into registers: o[q] = O[r0 + lr + 4q][c0 + lc] (natural layout).  For
+// a tall matrix the tile is staged through LDS so that the HBM reads stay
+// coalesced.  Every thread of the block must call it.
+template <typename UT>
+__device__ __forceinline__ f32x16_t load_nat_tile(const MatDev& md, const UT* X, int r0, int c0,
+                                                  float (&tile)[kEwTile][kEwTile + 1]) {
+  f32x16_t o;
+  const NatDims nd = nat_dims(md);
+  const int lc = threadIdx.x & 63, lr = threadIdx.x >> 6;
+  if (!md.trans) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      o[q] = Elem<UT>::ld(X, static_cast<int64_t>(r0 + lr + 4 * q) * nd.cp + c0 + lc);
+  } else {
+    // X[c][r]: read rows c0.. of X along r, transpose in LDS
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int cc = lr + 4 * q;
+      tile[cc][lc] = Elem<UT>::ld(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + lc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) o[q] = tile[lc][lr + 4 * q];
+  }
+  return o;
 }
 
 __global__ __launch_bounds__(256) void k_norm_finalize(const MatDev* __restrict__ mats,
@@ -138,46 +170,45 @@ __global__ __launch_bounds__(256) void k_apply(const MatDev* __restrict__ mats,
                                                const Item* __restrict__ items,
                                                PT* __restrict__ params, const UT* __restrict__ ws,
                                                const float* __restrict__ inv, int use_inv,
-                                               int xt_final, float lr, float wd, int scale_mode,
+                                               int x_final, float lr, float wd, int scale_mode,
                                                float rms_target, float* __restrict__ out_update) {
+  __shared__ float tile[kEwTile][kEwTile + 1];
   const Item it = items[blockIdx.x];
   const MatDev md = mats[it.mat];
   const int r0 = (it.rc >> 16) * kEwTile, c0 = (it.rc & 0xffff) * kEwTile;
-  const NatView nv = nat_view(md, xt_final);
-  const UT* nat = ws + nv.nat;
+  const f32x16_t o = load_nat_tile<UT>(md, ws + (x_final ? md.ws_x[1] : md.ws_x[0]), r0, c0, tile);
   const float osc = use_inv ? inv[md.widx] : 1.0f;
   const float decay = 1.0f - lr * wd;
   const float step = lr * update_scale(md.rows, md.cols, scale_mode, rms_target);
   const int c = c0 + (threadIdx.x & 63);
-  if (c >= md.cols) return;
-#pragma unroll 4
+#pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int r = r0 + (threadIdx.x >> 6) + 4 * q;
-    if (r >= md.rows) break;
-    const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
-    const float o = Elem<UT>::ld(nat, static_cast<int64_t>(r) * nv.cp + c) * osc;
-    const float w = Elem<PT>::ld(params, e);
-    Elem<PT>::st(params, e, decay * w - step * o);
-    if (out_update) out_update[e] = o;
+    if (r < md.rows && c < md.cols) {
+      const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
+      const float oo = o[q] * osc;
+      const float w = Elem<PT>::ld(params, e);
+      Elem<PT>::st(params, e, decay * w - step * oo);
+      if (out_update) out_update[e] = oo;
+    }
   }
 }
 
 template <typename UT>
 __global__ __launch_bounds__(256) void k_export(const MatDev* __restrict__ mats,
                                                 const Item* __restrict__ items,
-                                                const UT* __restrict__ ws, int xt_idx,
+                                                const UT* __restrict__ ws, int x_idx,
                                                 float* __restrict__ out) {
+  __shared__ float tile[kEwTile][kEwTile + 1];
   const Item it = items[blockIdx.x];
   const MatDev md = mats[it.mat];
   const int r0 = (it.rc >> 16) * kEwTile, c0 = (it.rc & 0xffff) * kEwTile;
-  const NatView nv = nat_view(md, xt_idx);
+  const f32x16_t o = load_nat_tile<UT>(md, ws + (x_idx ? md.ws_x[1] : md.ws_x[0]), r0, c0, tile);
   const int c = c0 + (threadIdx.x & 63);
-  if (c >= md.cols) return;
+#pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int r = r0 + (threadIdx.x >> 6) + 4 * q;
-    if (r >= md.rows) break;
-    out[md.off + static_cast<int64_t>(r) * md.cols + c] =
-        Elem<UT>::ld(ws + nv.nat, static_cast<int64_t>(r) * nv.cp + c);
+    if (r < md.rows && c < md.cols) out[md.off + static_cast<int64_t>(r) * md.cols + c] = o[q];
   }
 }
 
@@ -337,14 +368,14 @@ hipError_t launch_norm_finalize(const MatDev* mats, int mat_begin, int n_mats,
 
 hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int param_dtype,
                         int ns_dtype, void* params, const void* ws, const float* inv,
-                        float o_scale_by_inv, int xt_final, float lr, float wd, int scale_mode,
+                        float o_scale_by_inv, int x_final, float lr, float wd, int scale_mode,
                         float rms_target, float* out_update, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items), block(256);
   const int use_inv = o_scale_by_inv != 0.0f;
 #define MUON_K7(PT, UT)                                                                       \
   hipLaunchKernelGGL((k_apply<PT, UT>), grid, block, 0, s, mats, items, static_cast<PT*>(params), \
-                     static_cast<const UT*>(ws), inv, use_inv, xt_final, lr, wd, scale_mode,    \
+                     static_cast<const UT*>(ws), inv, use_inv, x_final, lr, wd, scale_mode,     \
                      rms_target, out_update)
   if (param_dtype == 1 && ns_dtype == 1) MUON_K7(uint16_t, uint16_t);
   else if (param_dtype == 1 && ns_dtype == 0) MUON_K7(uint16_t, float);
@@ -355,14 +386,14 @@ hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int 
 }
 
 hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int ns_dtype,
-                         const void* ws, int xt_idx, float* out, hipStream_t s) {
+                         const void* ws, int x_idx, float* out, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   if (ns_dtype == 1)
     hipLaunchKernelGGL((k_export<uint16_t>), dim3(n_items), dim3(256), 0, s, mats, items,
-                       static_cast<const uint16_t*>(ws), xt_idx, out);
+                       static_cast<const uint16_t*>(ws), x_idx, out);
   else
     hipLaunchKernelGGL((k_export<float>), dim3(n_items), dim3(256), 0, s, mats, items,
-                       static_cast<const float*>(ws), xt_idx, out);
+                       static_cast<const float*>(ws), x_idx, out);
   return hipGetLastError();
 }
 

@@ -70,11 +70,47 @@ size_t ns_elem_bytes(int ns_dtype) { return ns_dtype == MUON_DTYPE_BF16 ? 2 : 4;
 
 bool dtype_ok(int32_t d) { return d == MUON_DTYPE_FP32 || d == MUON_DTYPE_BF16; }
 
-// Per-matrix workspace elements (NS dtype): X, X^T x2, A, B.
+// Per-matrix workspace elements (NS dtype): X ping-pong, A, B.
 int64_t matrix_ws_elems(const MatDev& m) {
   const int64_t mn = static_cast<int64_t>(m.m_pad) * m.n_pad;
   const int64_t mm = static_cast<int64_t>(m.m_pad) * m.m_pad;
-  return 3 * mn + 2 * mm;
+  return 2 * mn + 2 * mm;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on
+// XCD b % 8), and each XCD has its own L2.  Tiles that share operand
+// panels should therefore run on the same XCD at the same time: the
+// logical list is cut into groups of kGroup tiles (one group ~ the 32 CUs
+// of an XCD), group s goes to XCD s % 8, and within an XCD the groups run
+// in logical order.  The list is padded with empty items (mat = -1) to a
+// multiple of 8 * kGroup; those workgroups exit at once.
+constexpr int kXcds = 8;
+constexpr int kGroup = 32;
+constexpr int kSuperRows = 4, kSuperCols = 8;
+
+std::vector<Item> xcd_dispatch_order(const std::vector<Item>& logical) {
+  const int64_t n = static_cast<int64_t>(logical.size());
+  if (n == 0) return {};
+  const int64_t round = static_cast<int64_t>(kXcds) * kGroup;
+  const int64_t padded = (n + round - 1) / round * round;
+  std::vector<Item> out(static_cast<size_t>(padded), Item{-1, 0});
+  for (int64_t b = 0; b < padded; ++b) {
+    const int64_t x = b % kXcds, l = b / kXcds;
+    const int64_t li = ((l / kGroup) * kXcds + x) * kGroup + (l % kGroup);
+    if (li < n) out[static_cast<size_t>(b)] = logical[static_cast<size_t>(li)];
+  }
+  return out;
+}
+
+// Tiles of one matrix (rows x cols tiles; upper triangle only if tri) in
+// super-tile order: kSuperRows x kSuperCols blocks, row-major, so that
+// consecutive tiles share their row and column operand panels.
+void emit_super_tiles(int mat, int rows, int cols, bool tri, std::vector<Item>& out) {
+  for (int R = 0; R < rows; R += kSuperRows)
+    for (int C = tri ? (R / kSuperCols) * kSuperCols : 0; C < cols; C += kSuperCols)
+      for (int a = R; a < std::min(rows, R + kSuperRows); ++a)
+        for (int b = C; b < std::min(cols, C + kSuperCols); ++b)
+          if (!tri || a <= b) out.push_back(Item{mat, (a << 16) | b});
 }
 
 // Build every host-side table; no HIP call.
@@ -197,11 +233,10 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
       const int64_t mn = static_cast<int64_t>(d.m_pad) * d.n_pad;
       const int64_t mm = static_cast<int64_t>(d.m_pad) * d.m_pad;
       const int64_t base = static_cast<int64_t>(off / eb);
-      d.ws_x = base;
-      d.ws_xt[0] = base + mn;
-      d.ws_xt[1] = base + 2 * mn;
-      d.ws_a = base + 3 * mn;
-      d.ws_b = base + 3 * mn + mm;
+      d.ws_x[0] = base;
+      d.ws_x[1] = base + mn;
+      d.ws_a = base + 2 * mn;
+      d.ws_b = base + 2 * mn + mm;
       off += align_up(static_cast<size_t>(matrix_ws_elems(d)) * eb, kAlign);
       // elementwise tiles over the natural padded extent, row-major
       const int64_t rp = d.trans ? d.n_pad : d.m_pad, cp = d.trans ? d.m_pad : d.n_pad;
@@ -215,28 +250,28 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     w.bytes = off;
     ws_max = std::max(ws_max, off);
 
-    // GEMM tile lists, most expensive (longest K) first; within equal cost
-    // keep matrix-major, row-major order so neighbours share operand panels.
-    struct Keyed { int64_t cost; Item it; };
-    std::vector<Keyed> syrk, bx;
-    for (int m = w.mat_begin; m < w.mat_end; ++m) {
-      const MatDev& d = p.mats[m];
-      const int mt = d.m_pad / T, nt = d.n_pad / T;
-      for (int a = 0; a < mt; ++a)
-        for (int b = a; b < mt; ++b)
-          syrk.push_back({d.n_pad, Item{m, (a << 16) | b}});
-      for (int a = 0; a < mt; ++a)
-        for (int b = 0; b < nt; ++b) bx.push_back({d.m_pad, Item{m, (a << 16) | b}});
-    }
-    auto by_cost = [](const Keyed& x, const Keyed& y) { return x.cost > y.cost; };
-    std::stable_sort(syrk.begin(), syrk.end(), by_cost);
-    std::stable_sort(bx.begin(), bx.end(), by_cost);
+    // GEMM tile lists: matrices with the longest K first, each matrix's
+    // tiles in super-tile order, then permuted so that every XCD receives
+    // whole groups of neighbouring tiles (see xcd_dispatch_order).
+    std::vector<int> order;
+    for (int m = w.mat_begin; m < w.mat_end; ++m) order.push_back(m);
+    std::vector<Item> syrk_l, bx_l;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+      return p.mats[x].n_pad > p.mats[y].n_pad;
+    });
+    for (int m : order) emit_super_tiles(m, p.mats[m].m_pad / T, p.mats[m].m_pad / T, true, syrk_l);
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+      return p.mats[x].m_pad > p.mats[y].m_pad;
+    });
+    for (int m : order) emit_super_tiles(m, p.mats[m].m_pad / T, p.mats[m].n_pad / T, false, bx_l);
+    const std::vector<Item> syrk = xcd_dispatch_order(syrk_l);
+    const std::vector<Item> bx = xcd_dispatch_order(bx_l);
     w.syrk_begin = static_cast<int64_t>(p.syrk_items.size());
     w.syrk_count = static_cast<int64_t>(syrk.size());
-    for (auto& k : syrk) p.syrk_items.push_back(k.it);
+    p.syrk_items.insert(p.syrk_items.end(), syrk.begin(), syrk.end());
     w.bx_begin = static_cast<int64_t>(p.bx_items.size());
     w.bx_count = static_cast<int64_t>(bx.size());
-    for (auto& k : bx) p.bx_items.push_back(k.it);
+    p.bx_items.insert(p.bx_items.end(), bx.begin(), bx.end());
     if (w.k1_count > 0x7fffffff || w.syrk_count > 0x7fffffff || w.bx_count > 0x7fffffff)
       return fail(MUON_ERR_BAD_SHAPE, "too many tiles in one wave");
   }
@@ -318,8 +353,7 @@ muon::GemmArgs gemm_args(const muon_plan_t* p, const Wave& w, void* ws, const mu
   g.b = hp->ns_b;
   g.c = hp->ns_c;
   g.first = iter == 0;
-  g.last = iter == hp->ns_steps - 1;
-  g.xt_cur = iter & 1;
+  g.x_cur = iter & 1;
   return g;
 }
 

@@ -14,9 +14,9 @@ constexpr int kTileFp32 = 64;
 
 // One matrix of a plan, as the device sees it.  "Oriented" dims put the
 // short side first (m = min(rows, cols), n = max(rows, cols)); tall
-// matrices (rows > cols) are iterated transposed.  The natural layout
-// buffer holds the matrix as the caller stores it ([rows, cols], padded),
-// the transposed buffer holds its transpose.
+// matrices (rows > cols) are iterated transposed.  The NS iterate X is
+// kept oriented ([m_pad][n_pad], row-major, zero padded) in two ping-pong
+// buffers.
 struct MatDev {
   int64_t off;      // element offset in the flat params/grads/momentum
   int32_t rows, cols;
@@ -26,10 +26,9 @@ struct MatDev {
   int32_t k1_begin;      // first elementwise tile of this matrix (wave-local)
   int32_t k1_count;      // number of elementwise tiles of this matrix
   // element offsets (in NS elements) into the workspace
-  int64_t ws_x;          // X  : m_pad x n_pad, row-major (oriented iterate)
-  int64_t ws_xt[2];      // X^T: n_pad x m_pad, ping-pong
-  int64_t ws_a;          // A  : m_pad x m_pad
-  int64_t ws_b;          // B  : m_pad x m_pad
+  int64_t ws_x[2];       // X : m_pad x n_pad, ping-pong
+  int64_t ws_a;          // A : m_pad x m_pad
+  int64_t ws_b;          // B : m_pad x m_pad
 };
 
 // A tile work item: matrix index (plan-global) and packed tile coords.
@@ -45,8 +44,7 @@ struct GemmArgs {
   const float* inv;   // wave-local 1/(||U||_F + eps)
   float a, b, c;
   int32_t first;      // first NS iteration: fold the normalisation in
-  int32_t last;       // last NS iteration: only the natural layout is needed
-  int32_t xt_cur;     // X^T buffer read by phase 3 (written: 1 - xt_cur)
+  int32_t x_cur;      // X buffer read by phases 1 and 3 (phase 3 writes 1 - x_cur)
 };
 
 // kernel launchers (defined in the .hip files)
@@ -59,11 +57,11 @@ hipError_t launch_norm_finalize(const MatDev* mats, int mat_begin, int n_mats,
                                 float eps, hipStream_t s);
 hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int param_dtype,
                         int ns_dtype, void* params, const void* ws, const float* inv,
-                        float o_scale_by_inv, int xt_final, float lr, float wd,
+                        float o_scale_by_inv, int x_final, float lr, float wd,
                         int scale_mode, float rms_target, float* out_update,
                         hipStream_t s);
 hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int ns_dtype,
-                         const void* ws, int xt_idx, float* out, hipStream_t s);
+                         const void* ws, int x_idx, float* out, hipStream_t s);
 hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, const GemmArgs& args,
                            hipStream_t s);
 hipError_t launch_adamw(void* params, int param_dtype, float* master, const void* grads,

@@ -1,29 +1,40 @@
 // Grouped, ragged Newton-Schulz engine for gfx950.
 //
 // One NS iteration (optimizer tutorial, section 4.2, generalised to
-// X <- a X + (b A + c A A) X with A = X X^T) is three grouped launches over
+// X <- a X + (b A + c A A) X with A = X X^T) runs as grouped launches over
 // every matrix of a wave:
-//   phase 1  A = s2 * X X^T        symmetric: one triangle of tiles, each
-//                                  tile written to (i,j) and mirrored to (j,i)
-//   phase 2  B = b A + c A A       symmetric (A A = A A^T), same scheme
-//   phase 3  X <- xs*(a X + B X)   (with c == 0 the product is b*(A X))
+//   phase 1  A = s2 * X X^T          symmetric: upper-triangle tiles, each
+//                                    written at (i,j) and mirrored to (j,i)
+//   phase 2  B = a I + b A + c A A   symmetric (A A = A A^T), same scheme;
+//                                    skipped when c == 0, in which case
+//                                    phase 1 writes B = a I + b s2 X X^T
+//   phase 3  X' = xs * (B X)         the a X term is folded into B's diagonal
 // On the first iteration s2 = inv^2 and xs = inv, which folds the
-// Frobenius normalisation X0 = U/(||U||_F + eps) into the GEMM epilogues.
+// Frobenius normalisation X0 = U/(||U||_F + eps) into the epilogues.
+// X lives in two ping-pong buffers (m x n, row-major, zero padded).
 //
-// Every product is computed in "NT" form, C[i][j] = sum_k P[i][k] Q[j][k],
-// with both operands K-contiguous in HBM:
-//   phase 1: P = Q = X (m x n);  phase 2: P = Q = A;
-//   phase 3: P = B, Q = X^T (n x m), which is why the workspace keeps the
-//   iterate in both layouts.  Phase 3 writes X in place (each X tile is
-//   read only by the work item that rewrites it) and X^T into the other
-//   ping-pong buffer.
+// Phases 1 and 2 are "NT" products, C[i][j] = sum_k P[i][k] Q[j][k], with
+// both operands K-contiguous.  Phase 3 is "NN": P = B (K-contiguous rows),
+// Q = X stored [k][j]; its MFMA fragments (8 consecutive k of one column)
+// are read from LDS with ds_read_b64_tr_b16, so no transposed copy of X is
+// ever written.
 //
 // bf16 engine: 256x256 tiles, BK = 64, 256 threads = 4 waves in a 2x2
 // grid, 128x128 per wave as 4x4 blocks of v_mfma_f32_32x32x16_bf16 with
-// fp32 accumulation; operands double-buffered in LDS (2 x 64 KiB) with an
-// XOR swizzle of the 16-byte chunks, so both the global->LDS stores and
-// the per-lane fragment reads are free of bank conflicts.
-// fp32 engine (tolerance path): 64x64 tiles of plain FMA.
+// fp32 accumulation.  Operands stream HBM -> LDS with global_load_lds
+// (16 bytes per lane, no VGPR staging), double-buffered (2 x 64 KiB).
+// LDS has 64 banks (256 bytes per cycle), and the layouts are swizzled so
+// that the DMA writes, ds_read_b128 and the transpose reads are free of
+// bank conflicts:
+//   K-contiguous tile [256 rows][64 k]: 16-byte chunk c of row r at
+//     position c ^ ((r >> 1) & 7);
+//   [k][j] tile [64 k][256 j]: 32-column block q of row k at q ^ (k & 3).
+// The epilogue stages each wave's 128x128 result in LDS (8-byte slot s of
+// row i at s ^ g(i), g(i) = ((i & 3) << 3) | ((i >> 2) & 7)) and writes it
+// with 16-byte row stores; the symmetric mirror is read back transposed
+// with ds_read_b64_tr_b16 and also written in 16-byte pieces.
+//
+// fp32 engine (tolerance path): 64x64 tiles of plain FMA, same phases.
 #include "muon_internal.h"
 
 namespace muon {
@@ -31,72 +42,100 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_t;
+typedef __attribute__((address_space(1))) void* gbl_void_t;
 
 constexpr int BT = kTileBf16;  // 256
 constexpr int BK = 64;
 
-struct Operands {
-  const uint16_t* P;
-  const uint16_t* Q;
-  int ld;  // = K
-};
-
-template <int PHASE>
-__device__ __forceinline__ void phase_operands(const GemmArgs& g, const MatDev& md, int ti,
-                                               int tj, const uint16_t* ws, const uint16_t*& P,
-                                               const uint16_t*& Q, int& ld) {
-  if (PHASE == 1) {
-    ld = md.n_pad;
-    P = ws + md.ws_x + static_cast<int64_t>(ti) * BT * ld;
-    Q = ws + md.ws_x + static_cast<int64_t>(tj) * BT * ld;
-  } else if (PHASE == 2) {
-    ld = md.m_pad;
-    P = ws + md.ws_a + static_cast<int64_t>(ti) * BT * ld;
-    Q = ws + md.ws_a + static_cast<int64_t>(tj) * BT * ld;
-  } else {
-    ld = md.m_pad;
-    P = ws + (g.c != 0.0f ? md.ws_b : md.ws_a) + static_cast<int64_t>(ti) * BT * ld;
-    Q = ws + md.ws_xt[g.xt_cur] + static_cast<int64_t>(tj) * BT * ld;
-  }
+// 16 bytes per lane, HBM -> LDS; lane l's data lands at lds + 16*l.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_wave_uniform) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)lds_wave_uniform, 16, 0, 0);
 }
 
-__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  uint2 r;
-  r.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-  r.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
-  return r;
+// Transpose read: within each group of 16 lanes, lane l receives element
+// (l % 4) of the 8-byte blocks addressed by lanes 4q + l/4, q = 0..3.
+__device__ __forceinline__ s16x4_t ld_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)p);
 }
-__device__ __forceinline__ void unpack4(uint2 r, float* o) {
-  o[0] = __uint_as_float(r.x << 16);
-  o[1] = __uint_as_float(r.x & 0xffff0000u);
-  o[2] = __uint_as_float(r.y << 16);
-  o[3] = __uint_as_float(r.y & 0xffff0000u);
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// staging layout of a wave's 128x128 bf16 result: element offset of the
+// 4-element (8-byte) slot holding (i, j..j+3), j % 4 == 0
+__device__ __forceinline__ int stg(int i, int j) {
+  const int g = ((i & 3) << 3) | ((i >> 2) & 7);
+  return i * 128 + ((((j >> 2) ^ g) & 31) << 2);
 }
 
 template <int PHASE>
 __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * BT * BK];  // 128 KiB
   const Item it = g.items[blockIdx.x];
+  if (it.mat < 0) return;  // padding of the XCD-grouped dispatch order
   const MatDev md = g.mats[it.mat];
   const int ti = it.rc >> 16, tj = it.rc & 0xffff;
-  const uint16_t* ws = static_cast<const uint16_t*>(g.ws);
+  uint16_t* ws = static_cast<uint16_t*>(g.ws);
+
+  // operands
   const uint16_t *P, *Q;
-  int ld;
-  phase_operands<PHASE>(g, md, ti, tj, ws, P, Q, ld);
+  int ldp, ldq, K;
+  if (PHASE == 1) {
+    ldp = ldq = K = md.n_pad;
+    P = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(ti) * BT * ldp;
+    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * BT * ldq;
+  } else if (PHASE == 2) {
+    ldp = ldq = K = md.m_pad;
+    P = ws + md.ws_a + static_cast<int64_t>(ti) * BT * ldp;
+    Q = ws + md.ws_a + static_cast<int64_t>(tj) * BT * ldq;
+  } else {
+    ldp = K = md.m_pad;
+    ldq = md.n_pad;
+    P = ws + md.ws_b + static_cast<int64_t>(ti) * BT * ldp;
+    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * BT;  // column block of [k][j]
+  }
 
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int wi = wv & 1, wj = wv >> 1;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wi = wave & 1, wj = wave >> 1;
+  const int frow = lane & 31;
 
-  // global -> LDS mapping: 8 threads per 128-byte row segment, 32 rows per
-  // pass, 8 passes per operand
-  const int lrow = t >> 3, lchunk = t & 7;
-  const int swz_st = (lchunk ^ (lrow & 7)) << 3;
-  const uint16_t* Pg = P + static_cast<int64_t>(lrow) * ld + lchunk * 8;
-  const uint16_t* Qg = Q + static_cast<int64_t>(lrow) * ld + lchunk * 8;
-  const int64_t row32 = static_cast<int64_t>(32) * ld;
+  // DMA of one K stage into buffer `buf`: 32 instructions of 1 KiB per
+  // operand, 8 per wave.
+  auto load_stage = [&](int kt, int buf) {
+    uint16_t* sp = smem + buf * 2 * BT * BK;
+    uint16_t* sq = sp + BT * BK;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int R0 = (wave * 8 + u) * 8;  // 8 rows of 128 bytes
+      const int row = R0 + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      dma16(P + static_cast<int64_t>(row) * ldp + k0 + 8 * c, sp + R0 * BK);
+      if (PHASE != 3)
+        dma16(Q + static_cast<int64_t>(row) * ldq + k0 + 8 * c, sq + R0 * BK);
+    }
+    if (PHASE == 3) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int R0 = (wave * 8 + u) * 2;  // 2 k-rows of 512 bytes
+        const int row = R0 + (lane >> 5);
+        const int c = (lane & 31) ^ ((row & 3) << 2);
+        dma16(Q + static_cast<int64_t>(k0 + row) * ldq + 8 * c, sq + R0 * BT);
+      }
+    }
+  };
 
-  u32x4_t rp[8], rq[8];
   f32x16_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -105,43 +144,40 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    rp[r] = *reinterpret_cast<const u32x4_t*>(Pg + r * row32);
-    rq[r] = *reinterpret_cast<const u32x4_t*>(Qg + r * row32);
-  }
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    *reinterpret_cast<u32x4_t*>(smem + (lrow + 32 * r) * BK + swz_st) = rp[r];
-    *reinterpret_cast<u32x4_t*>(smem + BT * BK + (lrow + 32 * r) * BK + swz_st) = rq[r];
-  }
+  load_stage(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  const int nk = ld / BK;
-  const int frow = lane & 31;
+  const int nk = K / BK;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = (kt + 1) * BK;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        rp[r] = *reinterpret_cast<const u32x4_t*>(Pg + r * row32 + k0);
-        rq[r] = *reinterpret_cast<const u32x4_t*>(Qg + r * row32 + k0);
-      }
-    }
+    if (kt + 1 < nk) load_stage(kt + 1, buf ^ 1);
     const uint16_t* sp = smem + buf * 2 * BT * BK;
     const uint16_t* sq = sp + BT * BK;
-    // fragments of k-substep ks+1 are read from LDS while the 16 MFMAs of
-    // substep ks run
+    // fragments of k-substep ks+1 are read while the MFMAs of ks run
     bf16x8_t qf[2][4], pf[2][4];
     auto read_frags = [&](int ks, bf16x8_t* q, bf16x8_t* p) {
       const int kc = ks * 2 + (lane >> 5);
-      const int sw = (kc ^ (lane & 7)) << 3;
+      const int sw = (kc ^ ((frow >> 1) & 7)) << 3;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        q[b] = *reinterpret_cast<const bf16x8_t*>(sq + (wj * 128 + b * 32 + frow) * BK + sw);
+      for (int b = 0; b < 4; ++b)
         p[b] = *reinterpret_cast<const bf16x8_t*>(sp + (wi * 128 + b * 32 + frow) * BK + sw);
+      if (PHASE != 3) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          q[b] = *reinterpret_cast<const bf16x8_t*>(sq + (wj * 128 + b * 32 + frow) * BK + sw);
+      } else {
+        const int s = lane & 15;
+        const int kr = ks * 16 + 8 * (lane >> 5) + (s >> 2);
+        const int sx = (kr & 3) << 5;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int col = (wj * 128 + b * 32 + 16 * ((lane >> 4) & 1) + 4 * (s & 3)) ^ sx;
+          const s16x4_t lo = ld_tr(sq + kr * BT + col);
+          const s16x4_t hi = ld_tr(sq + (kr + 4) * BT + col);
+          q[b] = __builtin_bit_cast(bf16x8_t,
+                                    __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       }
     };
     read_frags(0, qf[0], pf[0]);
@@ -158,86 +194,109 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
                                                                 acc[bj][bi], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      uint16_t* dp = smem + (buf ^ 1) * 2 * BT * BK;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        *reinterpret_cast<u32x4_t*>(dp + (lrow + 32 * r) * BK + swz_st) = rp[r];
-        *reinterpret_cast<u32x4_t*>(dp + BT * BK + (lrow + 32 * r) * BK + swz_st) = rq[r];
-      }
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // ---- epilogue.  Accumulator layout of the 32x32 MFMA (A operand = Q
   // rows j, B operand = P rows i): lane holds column i = lane%32 and rows
   // j = 8*(v/4) + 4*(lane/32) + v%4, i.e. C[i][j..j+3] for each v/4.
-  uint16_t* wsw = static_cast<uint16_t*>(g.ws);
-  const int ib = ti * BT + wi * 128 + frow;
-  const int jb = tj * BT + wj * 128 + 4 * (lane >> 5);
+  // Wave sub-tile: rows i0w..i0w+127, columns j0w..j0w+127; LDS region of
+  // this wave: 32 KiB (the operand buffers are no longer needed).
+  uint16_t* S = smem + wave * (128 * 128);
+  const int i0w = ti * BT + wi * 128, j0w = tj * BT + wj * 128;
   const float inv = g.first ? g.inv[md.widx] : 1.0f;
-  if (PHASE == 1 || PHASE == 2) {
-    const int ldc = md.m_pad;
-    uint16_t* C = wsw + (PHASE == 1 ? md.ws_a : md.ws_b);
-    const uint16_t* Aold = wsw + md.ws_a;
-    const float s2 = inv * inv;
-    const bool mirror = ti != tj;
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = ib + bi * 32;
-          const int j = jb + bj * 32 + 8 * q;
-          float v[4];
-          if (PHASE == 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = s2 * acc[bj][bi][4 * q + e];
-          } else {
-            float a0[4];
-            unpack4(*reinterpret_cast<const uint2*>(Aold + static_cast<int64_t>(i) * ldc + j), a0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = g.b * a0[e] + g.c * acc[bj][bi][4 * q + e];
-          }
-          const uint2 pk = pack4(v[0], v[1], v[2], v[3]);
-          *reinterpret_cast<uint2*>(C + static_cast<int64_t>(i) * ldc + j) = pk;
-          if (mirror) {
-            C[static_cast<int64_t>(j + 0) * ldc + i] = static_cast<uint16_t>(pk.x & 0xffffu);
-            C[static_cast<int64_t>(j + 1) * ldc + i] = static_cast<uint16_t>(pk.x >> 16);
-            C[static_cast<int64_t>(j + 2) * ldc + i] = static_cast<uint16_t>(pk.y & 0xffffu);
-            C[static_cast<int64_t>(j + 3) * ldc + i] = static_cast<uint16_t>(pk.y >> 16);
-          }
-        }
+  uint16_t* C;
+  int ldc;
+  bool mirror;
+  if (PHASE == 3) {
+    C = ws + (g.x_cur ? md.ws_x[0] : md.ws_x[1]);
+    ldc = md.n_pad;
+    mirror = false;
   } else {
-    const int ldx = md.n_pad, ldt = md.m_pad;
-    uint16_t* X = wsw + md.ws_x;
-    uint16_t* XT = wsw + md.ws_xt[g.xt_cur ^ 1];
-    const float alpha = g.c != 0.0f ? 1.0f : g.b;
-    const bool write_x = !(g.last && md.trans);
-    const bool write_xt = !(g.last && !md.trans);
+    C = ws + ((PHASE == 1 && g.c != 0.0f) ? md.ws_a : md.ws_b);
+    ldc = md.m_pad;
+    mirror = ti != tj;
+  }
+
+  if (PHASE == 2) {
+    // b*A term: stage this wave's A sub-tile in LDS (16-byte row loads)
+    const uint16_t* Ao = ws + md.ws_a;
+#pragma unroll 8
+    for (int u = 0; u < 32; ++u) {
+      const int r = (lane >> 4) + 4 * u, c = lane & 15;
+      u32x4_t v = *reinterpret_cast<const u32x4_t*>(Ao + static_cast<int64_t>(i0w + r) * ldc +
+                                                    j0w + 8 * c);
+      const int o0 = stg(r, 8 * c), o1 = stg(r, 8 * c + 4);
+      *reinterpret_cast<u32x2_t*>(S + o0) = u32x2_t{v[0], v[1]};
+      *reinterpret_cast<u32x2_t*>(S + o1) = u32x2_t{v[2], v[3]};
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // values -> LDS staging (8-byte slots)
+  const float s2 = inv * inv;
+  const bool diag = ti == tj && PHASE != 3;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+  for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = ib + bi * 32;
-          const int j = jb + bj * 32 + 8 * q;
-          float x0[4], v[4];
-          uint16_t* xp = X + static_cast<int64_t>(i) * ldx + j;
-          unpack4(*reinterpret_cast<const uint2*>(xp), x0);
+      for (int q = 0; q < 4; ++q) {
+        const int il = bi * 32 + frow;
+        const int jl = bj * 32 + 8 * q + 4 * (lane >> 5);
+        const int o = stg(il, jl);
+        f32x4_t v;
+        if (PHASE == 1) {
+          const float bb = g.c != 0.0f ? 1.0f : g.b;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = inv * (g.a * x0[e] + alpha * acc[bj][bi][4 * q + e]);
-          const uint2 pk = pack4(v[0], v[1], v[2], v[3]);
-          if (write_x) *reinterpret_cast<uint2*>(xp) = pk;
-          if (write_xt) {
-            XT[static_cast<int64_t>(j + 0) * ldt + i] = static_cast<uint16_t>(pk.x & 0xffffu);
-            XT[static_cast<int64_t>(j + 1) * ldt + i] = static_cast<uint16_t>(pk.x >> 16);
-            XT[static_cast<int64_t>(j + 2) * ldt + i] = static_cast<uint16_t>(pk.y & 0xffffu);
-            XT[static_cast<int64_t>(j + 3) * ldt + i] = static_cast<uint16_t>(pk.y >> 16);
-          }
+          for (int e = 0; e < 4; ++e) v[e] = bb * s2 * acc[bj][bi][4 * q + e];
+        } else if (PHASE == 2) {
+          const u32x2_t a0 = *reinterpret_cast<const u32x2_t*>(S + o);
+          const f32x4_t ao = {lo_bf(a0[0]), hi_bf(a0[0]), lo_bf(a0[1]), hi_bf(a0[1])};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = g.b * ao[e] + g.c * acc[bj][bi][4 * q + e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = inv * acc[bj][bi][4 * q + e];
         }
+        if (diag && (PHASE == 2 || g.c == 0.0f)) {
+          // a on the diagonal of B
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (i0w + il == j0w + jl + e) v[e] += g.a;
+        }
+        *reinterpret_cast<u32x2_t*>(S + o) = u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      }
+  __builtin_amdgcn_wave_barrier();
+
+  // row stores: 16 bytes per lane, 4 rows of 256 bytes per instruction
+#pragma unroll 8
+  for (int u = 0; u < 32; ++u) {
+    const int r = (lane >> 4) + 4 * u, c = lane & 15;
+    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(S + stg(r, 8 * c));
+    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(S + stg(r, 8 * c + 4));
+    *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(i0w + r) * ldc + j0w + 8 * c) =
+        u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  }
+
+  if (mirror) {
+    // C^T[j][i..i+7] = C[i..i+7][j] via two transpose reads per lane:
+    // group G = lane/16 covers columns jb + 16*(G&1) + (lane%16) and rows
+    // ib + 8*(G>>1) .. +7 of the staged tile.
+    const int s = lane & 15, G = lane >> 4;
+#pragma unroll 4
+    for (int u = 0; u < 32; ++u) {
+      const int jb = (u & 3) * 32, ib = (u >> 2) * 16;
+      const int ir = ib + 8 * (G >> 1) + (s >> 2);
+      const int jc = jb + 16 * (G & 1) + 4 * (s & 3);
+      const s16x4_t lo = ld_tr(S + stg(ir, jc));
+      const s16x4_t hi = ld_tr(S + stg(ir + 4, jc));
+      const int jo = jb + 16 * (G & 1) + s;
+      const int io = ib + 8 * (G >> 1);
+      *reinterpret_cast<s16x8_t*>(C + static_cast<int64_t>(j0w + jo) * ldc + i0w + io) =
+          __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
   }
 }
 
@@ -251,98 +310,93 @@ __global__ __launch_bounds__(256) void k_ns_f32(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float Ps[FK][FT + 4];
   __shared__ __attribute__((aligned(16))) float Qs[FK][FT + 4];
   const Item it = g.items[blockIdx.x];
+  if (it.mat < 0) return;  // padding of the XCD-grouped dispatch order
   const MatDev md = g.mats[it.mat];
   const int ti = it.rc >> 16, tj = it.rc & 0xffff;
   float* ws = static_cast<float*>(g.ws);
   const float *P, *Q;
-  int ld;
+  int ldp, ldq, K;
   if (PHASE == 1) {
-    ld = md.n_pad;
-    P = ws + md.ws_x + static_cast<int64_t>(ti) * FT * ld;
-    Q = ws + md.ws_x + static_cast<int64_t>(tj) * FT * ld;
+    ldp = ldq = K = md.n_pad;
+    P = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(ti) * FT * ldp;
+    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * FT * ldq;
   } else if (PHASE == 2) {
-    ld = md.m_pad;
-    P = ws + md.ws_a + static_cast<int64_t>(ti) * FT * ld;
-    Q = ws + md.ws_a + static_cast<int64_t>(tj) * FT * ld;
+    ldp = ldq = K = md.m_pad;
+    P = ws + md.ws_a + static_cast<int64_t>(ti) * FT * ldp;
+    Q = ws + md.ws_a + static_cast<int64_t>(tj) * FT * ldq;
   } else {
-    ld = md.m_pad;
-    P = ws + (g.c != 0.0f ? md.ws_b : md.ws_a) + static_cast<int64_t>(ti) * FT * ld;
-    Q = ws + md.ws_xt[g.xt_cur] + static_cast<int64_t>(tj) * FT * ld;
+    ldp = K = md.m_pad;
+    ldq = md.n_pad;
+    P = ws + md.ws_b + static_cast<int64_t>(ti) * FT * ldp;
+    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * FT;  // [k][j] column block
   }
   const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-  const int lrow = t >> 2, lk = (t & 3) * 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < ld; k0 += FK) {
-    const float4 pv = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(lrow) * ld + k0 + lk);
-    const float4 qv = *reinterpret_cast<const float4*>(Q + static_cast<int64_t>(lrow) * ld + k0 + lk);
+  const int lrow = t >> 2, lk = (t & 3) * 4;      // K-contiguous loads
+  const int qk = t >> 4, qj = (t & 15) * 4;       // [k][j] loads (phase 3)
+  f32x16_t acc = {};
+  for (int k0 = 0; k0 < K; k0 += FK) {
+    const float4 pv = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(lrow) * ldp + k0 + lk);
+    float4 qv;
+    if (PHASE != 3)
+      qv = *reinterpret_cast<const float4*>(Q + static_cast<int64_t>(lrow) * ldq + k0 + lk);
+    else
+      qv = *reinterpret_cast<const float4*>(Q + static_cast<int64_t>(k0 + qk) * ldq + qj);
     __syncthreads();
     Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
-    Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
+    if (PHASE != 3) {
+      Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
+    } else {
+      *reinterpret_cast<float4*>(&Qs[qk][qj]) = qv;
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < FK; ++k) {
-      const float4 pa = *reinterpret_cast<const float4*>(&Ps[k][ty * 4]);
-      const float4 qa = *reinterpret_cast<const float4*>(&Qs[k][tx * 4]);
-      const float p4[4] = {pa.x, pa.y, pa.z, pa.w};
-      const float q4[4] = {qa.x, qa.y, qa.z, qa.w};
+      const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(&Ps[k][ty * 4]);
+      const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(&Qs[k][tx * 4]);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(p4[a], q4[b], acc[a][b]);
+        for (int b = 0; b < 4; ++b) acc[4 * a + b] = fmaf(p4[a], q4[b], acc[4 * a + b]);
     }
   }
   const float inv = g.first ? g.inv[md.widx] : 1.0f;
   const int i0 = ti * FT + ty * 4, j0 = tj * FT + tx * 4;
-  if (PHASE == 1 || PHASE == 2) {
-    const int ldc = md.m_pad;
-    float* C = ws + (PHASE == 1 ? md.ws_a : md.ws_b);
-    const float* Aold = ws + md.ws_a;
-    const float s2 = inv * inv;
-    float v[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (PHASE == 2) a0 = *reinterpret_cast<const float4*>(Aold + static_cast<int64_t>(i0 + a) * ldc + j0);
-      const float ao[4] = {a0.x, a0.y, a0.z, a0.w};
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        v[a][b] = PHASE == 1 ? s2 * acc[a][b] : g.b * ao[b] + g.c * acc[a][b];
-    }
+  f32x16_t v;
+  if (PHASE == 3) {
+    float* X = ws + (g.x_cur ? md.ws_x[0] : md.ws_x[1]);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      *reinterpret_cast<float4*>(C + static_cast<int64_t>(i0 + a) * ldc + j0) =
-          make_float4(v[a][0], v[a][1], v[a][2], v[a][3]);
-    if (ti != tj) {
+      *reinterpret_cast<float4*>(X + static_cast<int64_t>(i0 + a) * md.n_pad + j0) =
+          make_float4(inv * acc[4 * a], inv * acc[4 * a + 1], inv * acc[4 * a + 2],
+                      inv * acc[4 * a + 3]);
+    return;
+  }
+  const int ldc = md.m_pad;
+  float* C = ws + ((PHASE == 1 && g.c != 0.0f) ? md.ws_a : md.ws_b);
+  const float* Aold = ws + md.ws_a;
+  const float s2 = inv * inv;
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        *reinterpret_cast<float4*>(C + static_cast<int64_t>(j0 + b) * ldc + i0) =
-            make_float4(v[0][b], v[1][b], v[2][b], v[3][b]);
+  for (int a = 0; a < 4; ++a) {
+    f32x4_t ao = {0.f, 0.f, 0.f, 0.f};
+    if (PHASE == 2) ao = *reinterpret_cast<const f32x4_t*>(Aold + static_cast<int64_t>(i0 + a) * ldc + j0);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float x;
+      if (PHASE == 1) x = (g.c != 0.0f ? 1.0f : g.b) * s2 * acc[4 * a + b];
+      else x = g.b * ao[b] + g.c * acc[4 * a + b];
+      if ((PHASE == 2 || g.c == 0.0f) && i0 + a == j0 + b) x += g.a;
+      v[4 * a + b] = x;
     }
-  } else {
-    const int ldx = md.n_pad, ldt = md.m_pad;
-    float* X = ws + md.ws_x;
-    float* XT = ws + md.ws_xt[g.xt_cur ^ 1];
-    const float alpha = g.c != 0.0f ? 1.0f : g.b;
-    float v[4][4];
+  }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const float4 x0 = *reinterpret_cast<const float4*>(X + static_cast<int64_t>(i0 + a) * ldx + j0);
-      const float xo[4] = {x0.x, x0.y, x0.z, x0.w};
+  for (int a = 0; a < 4; ++a)
+    *reinterpret_cast<float4*>(C + static_cast<int64_t>(i0 + a) * ldc + j0) =
+        make_float4(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
+  if (ti != tj) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) v[a][b] = inv * (g.a * xo[b] + alpha * acc[a][b]);
-    }
-    if (!(g.last && md.trans)) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<float4*>(X + static_cast<int64_t>(i0 + a) * ldx + j0) =
-            make_float4(v[a][0], v[a][1], v[a][2], v[a][3]);
-    }
-    if (!(g.last && !md.trans)) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        *reinterpret_cast<float4*>(XT + static_cast<int64_t>(j0 + b) * ldt + i0) =
-            make_float4(v[0][b], v[1][b], v[2][b], v[3][b]);
-    }
+    for (int b = 0; b < 4; ++b)
+      *reinterpret_cast<float4*>(C + static_cast<int64_t>(j0 + b) * ldc + i0) =
+          make_float4(v[b], v[4 + b], v[8 + b], v[12 + b]);
   }
 }
 

@@ -60,16 +60,16 @@ def test_workspace_size_validation():
 
 def test_workspace_size_layout():
     # bf16 NS pads to 256: a 300x100 (tall) matrix is oriented 100x300 ->
-    # m_pad 256, n_pad 512; X, X^T x2 (3*256*512) and A, B (2*256*256), bf16.
+    # m_pad 256, n_pad 512; X ping-pong (2*256*512) and A, B (2*256*256), bf16.
     b = M.muon_workspace_size([(0, 300, 100)], 30000, "bf16", "bf16", "bf16")
     k1 = (512 // 64) * (256 // 64)
     fixed = 256 + 256 + 256  # partials (k1*4 <= 256), norms, inverse norms
     assert k1 * 4 <= 256
-    assert b == fixed + 2 * (3 * 256 * 512 + 2 * 256 * 256)
-    # fp32 NS pads to 64: 128x256 -> X, X^T x2 and A, B in fp32
+    assert b == fixed + 2 * (2 * 256 * 512 + 2 * 256 * 256)
+    # fp32 NS pads to 64: 128x256 -> X ping-pong and A, B in fp32
     b = M.muon_workspace_size([(0, 128, 256)], 128 * 256, "fp32", "fp32", "fp32")
     k1 = 2 * 4
-    assert b == 256 * 3 + 4 * (3 * 128 * 256 + 2 * 128 * 128)
+    assert b == 256 * 3 + 4 * (2 * 128 * 256 + 2 * 128 * 128)
     # empty plan
     assert M.muon_workspace_size([], 0, "bf16", "bf16", "bf16") == 0
 
