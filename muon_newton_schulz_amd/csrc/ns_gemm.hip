@@ -19,22 +19,26 @@
 // are read from LDS with ds_read_b64_tr_b16, so no transposed copy of X is
 // ever written.
 //
-// bf16 engine: 256x256 tiles, BK = 64, 256 threads = 4 waves in a 2x2
-// grid, 128x128 per wave as 4x4 blocks of v_mfma_f32_32x32x16_bf16 with
-// fp32 accumulation.  Operands stream HBM -> LDS with global_load_lds
-// (16 bytes per lane, no VGPR staging), double-buffered (2 x 64 KiB).
+// bf16 engine: 256x256 tiles, 256 threads = 4 waves in a 2x2 grid,
+// 128x128 per wave as 4x4 blocks of v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation.  Operands stream HBM -> LDS with global_load_lds (16 bytes
+// per lane, no VGPR staging) through a ring of 4 slots of 32 K-columns
+// (4 x 32 KiB), three stages in flight: the operand loads see L2 latencies
+// of several hundred cycles and one stage in flight cannot cover them.
 // LDS has 64 banks (256 bytes per cycle), and the layouts are swizzled so
 // that the DMA writes, ds_read_b128 and the transpose reads are free of
 // bank conflicts:
-//   K-contiguous tile [256 rows][64 k]: 16-byte chunk c of row r at
-//     position c ^ ((r >> 1) & 7);
-//   [k][j] tile [64 k][256 j]: 32-column block q of row k at q ^ (k & 3).
+//   K-contiguous tile [256 rows][32 k]: 16-byte chunk c of row r at
+//     position c ^ ((r >> 2) & 3);
+//   [k][j] tile [32 k][256 j]: 32-column block q of row k at q ^ (k & 3).
 // The epilogue stages each wave's 128x128 result in LDS (8-byte slot s of
 // row i at s ^ g(i), g(i) = ((i & 3) << 3) | ((i >> 2) & 7)) and writes it
 // with 16-byte row stores; the symmetric mirror is read back transposed
 // with ds_read_b64_tr_b16 and also written in 16-byte pieces.
 //
 // fp32 engine (tolerance path): 64x64 tiles of plain FMA, same phases.
+#include <type_traits>
+
 #include "muon_internal.h"
 
 namespace muon {
@@ -52,17 +56,61 @@ typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
 
 constexpr int BT = kTileBf16;  // 256
-constexpr int BK = 64;
+constexpr int BK = 32;           // K per pipeline stage
+constexpr int NSLOT = 4;         // LDS ring slots (stages in flight: NSLOT - 1)
+constexpr int DMA_PER_STAGE = 8;  // DMA instructions per wave per stage
 
 // 16 bytes per lane, HBM -> LDS; lane l's data lands at lds + 16*l.
 __device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_wave_uniform) {
   __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)lds_wave_uniform, 16, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t)p));
+}
+
 // Transpose read: within each group of 16 lanes, lane l receives element
 // (l % 4) of the 8-byte blocks addressed by lanes 4q + l/4, q = 0..3.
 __device__ __forceinline__ s16x4_t ld_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)p);
+}
+
+// Main-loop fragment reads are issued as inline asm: the compiler's
+// wait-count pass would otherwise make every transpose read wait for all
+// LDS DMA in flight (vmcnt(0)), which drains the load pipeline.  Their
+// completion is awaited explicitly with wait_frags before use.
+__device__ __forceinline__ s16x4_t ld_tr_async(const uint16_t* p) {
+  s16x4_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)) : "memory");
+  return r;
+}
+__device__ __forceinline__ bf16x8_t ld128_async(const uint16_t* p) {
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)) : "memory");
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+// Wait until this wave's DMA for stage `st` has landed, given that stages
+// up to `newest` have been issued (DMA_PER_STAGE instructions each); the
+// newer stages may stay in flight (vmcnt counts vector memory
+// instructions, which complete in issue order).
+__device__ __forceinline__ void wait_stage_landed(int st, int newest) {
+  const int newer = newest - st;
+  static_assert(DMA_PER_STAGE == 8, "wait counts below assume 8 DMA per stage");
+  if (newer >= 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (newer == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (newer == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Wait until at most N LDS reads are outstanding; the fragments are tied
+// to the wait so that their consumers cannot be scheduled above it.
+template <int N>
+__device__ __forceinline__ void wait_frags(bf16x8_t* q, bf16x8_t* p) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(p[0]), "+v"(p[1]),
+                 "+v"(p[2]), "+v"(p[3])
+               : "n"(N)
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -80,7 +128,7 @@ __device__ __forceinline__ int stg(int i, int j) {
 
 template <int PHASE>
 __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * BT * BK];  // 128 KiB
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * 2 * BT * BK];  // 128 KiB
   const Item it = g.items[blockIdx.x];
   if (it.mat < 0) return;  // padding of the XCD-grouped dispatch order
   const MatDev md = g.mats[it.mat];
@@ -110,29 +158,41 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
   const int wi = wave & 1, wj = wave >> 1;
   const int frow = lane & 31;
 
-  // DMA of one K stage into buffer `buf`: 32 instructions of 1 KiB per
-  // operand, 8 per wave.
-  auto load_stage = [&](int kt, int buf) {
-    uint16_t* sp = smem + buf * 2 * BT * BK;
-    uint16_t* sq = sp + BT * BK;
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int R0 = (wave * 8 + u) * 8;  // 8 rows of 128 bytes
-      const int row = R0 + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      dma16(P + static_cast<int64_t>(row) * ldp + k0 + 8 * c, sp + R0 * BK);
-      if (PHASE != 3)
-        dma16(Q + static_cast<int64_t>(row) * ldq + k0 + 8 * c, sq + R0 * BK);
+  // MFMA operand fragments.  A fragment set (one 16-wide k substep) is
+  // NR LDS reads: 4 P fragments (ds_read_b128) then the Q fragments, 4
+  // ds_read_b128 (phases 1, 2) or 8 transpose reads (phase 3, lo/hi halves
+  // of 8 consecutive k).  Read r of a set is issued by issue_read so that
+  // the reads can be interleaved one by one with MFMAs.
+  constexpr int NR = PHASE == 3 ? 12 : 8;
+  struct Frags {
+    bf16x8_t p[4];
+    bf16x8_t q[4];
+    s16x4_t t[8];  // phase 3: transposed halves of q
+  };
+  auto issue_read = [&](Frags& f, int slot, int ks, int r) {
+    const uint16_t* sp = smem + slot * 2 * BT * BK;
+    const uint16_t* sq = sp + BT * BK;
+    if (r < 4 || PHASE != 3) {
+      const int kc = ks * 2 + (lane >> 5);
+      const int sw = (kc ^ ((frow >> 2) & 3)) << 3;
+      if (r < 4) f.p[r] = ld128_async(sp + (wi * 128 + r * 32 + frow) * BK + sw);
+      else f.q[r - 4] = ld128_async(sq + (wj * 128 + (r - 4) * 32 + frow) * BK + sw);
+    } else {
+      const int b = (r - 4) >> 1, h = (r - 4) & 1;
+      const int s = lane & 15;
+      const int kr = ks * 16 + 8 * (lane >> 5) + (s >> 2) + 4 * h;
+      const int col = (wj * 128 + b * 32 + 16 * ((lane >> 4) & 1) + 4 * (s & 3)) ^ ((kr & 3) << 5);
+      f.t[r - 4] = ld_tr_async(sq + kr * BT + col);
     }
+  };
+  // all reads of a set have landed (no other LDS reads outstanding)
+  auto settle = [&](Frags& f) {
+    wait_frags<0>(f.q, f.p);
     if (PHASE == 3) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int R0 = (wave * 8 + u) * 2;  // 2 k-rows of 512 bytes
-        const int row = R0 + (lane >> 5);
-        const int c = (lane & 31) ^ ((row & 3) << 2);
-        dma16(Q + static_cast<int64_t>(k0 + row) * ldq + 8 * c, sq + R0 * BT);
-      }
+      for (int b = 0; b < 4; ++b)
+        f.q[b] = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(f.t[2 * b], f.t[2 * b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
 
@@ -144,59 +204,87 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  load_stage(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // DMA of one stage, one instruction at a time: instruction d (0..7) of
+  // this wave; d < 4: P rows, d >= 4: Q rows.
+  auto issue_dma = [&](int kt, int slot, int d) {
+    uint16_t* sp = smem + slot * 2 * BT * BK;
+    uint16_t* sq = sp + BT * BK;
+    const int k0 = kt * BK;
+    const int u = d & 3;
+    if (d < 4 || PHASE != 3) {
+      const int R0 = (wave * 4 + u) * 16;  // 16 rows of 64 bytes
+      const int row = R0 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      if (d < 4) dma16(P + static_cast<int64_t>(row) * ldp + k0 + 8 * c, sp + R0 * BK);
+      else dma16(Q + static_cast<int64_t>(row) * ldq + k0 + 8 * c, sq + R0 * BK);
+    } else {
+      const int R0 = (wave * 4 + u) * 2;  // 2 k-rows of 512 bytes
+      const int row = R0 + (lane >> 5);
+      const int c = (lane & 31) ^ ((row & 3) << 2);
+      dma16(Q + static_cast<int64_t>(k0 + row) * ldq + 8 * c, sq + R0 * BT);
+    }
+  };
+
+  // Pipeline: a ring of NSLOT stages, NSLOT - 1 in flight.  Per stage two
+  // groups of 16 MFMAs (k substeps 0 and 1).  Group A runs on substep 0
+  // while the reads of substep 1 are issued between its MFMAs.  Then this
+  // wave waits for its DMA of stage kt+1 and the workgroup barrier makes
+  // every wave's DMA visible and guarantees slot kt-1 is no longer read.
+  // Group B runs on substep 1 while the DMA of stage kt+NSLOT-1 (into slot
+  // kt-1) and the reads of stage kt+1's substep 0 are issued between its
+  // MFMAs.  Every memory instruction sits next to an MFMA, so the matrix
+  // pipe does not wait for instruction issue.
+  const int nk = K / BK;
+#pragma unroll
+  for (int s0 = 0; s0 < NSLOT - 1; ++s0)
+    if (s0 < nk)
+      for (int d = 0; d < DMA_PER_STAGE; ++d) issue_dma(s0, s0, d);
+  wait_stage_landed(0, min(NSLOT - 2, nk - 1));
   __syncthreads();
 
-  const int nk = K / BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_stage(kt + 1, buf ^ 1);
-    const uint16_t* sp = smem + buf * 2 * BT * BK;
-    const uint16_t* sq = sp + BT * BK;
-    // fragments of k-substep ks+1 are read while the MFMAs of ks run
-    bf16x8_t qf[2][4], pf[2][4];
-    auto read_frags = [&](int ks, bf16x8_t* q, bf16x8_t* p) {
-      const int kc = ks * 2 + (lane >> 5);
-      const int sw = (kc ^ ((frow >> 1) & 7)) << 3;
+  Frags F[2];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        p[b] = *reinterpret_cast<const bf16x8_t*>(sp + (wi * 128 + b * 32 + frow) * BK + sw);
-      if (PHASE != 3) {
+  for (int r = 0; r < NR; ++r) issue_read(F[0], 0, 0, r);
+
+  // one stage; REFILL: issue the DMA of stage kt+NSLOT-1, NEXT: read the
+  // first fragments of stage kt+1 (both true except in the last stages)
+  auto stage = [&](int kt, auto refill_c, auto next_c) {
+    constexpr bool REFILL = decltype(refill_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
+    const int slot = kt % NSLOT;
+    settle(F[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          q[b] = *reinterpret_cast<const bf16x8_t*>(sq + (wj * 128 + b * 32 + frow) * BK + sw);
-      } else {
-        const int s = lane & 15;
-        const int kr = ks * 16 + 8 * (lane >> 5) + (s >> 2);
-        const int sx = (kr & 3) << 5;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int col = (wj * 128 + b * 32 + 16 * ((lane >> 4) & 1) + 4 * (s & 3)) ^ sx;
-          const s16x4_t lo = ld_tr(sq + kr * BT + col);
-          const s16x4_t hi = ld_tr(sq + (kr + 4) * BT + col);
-          q[b] = __builtin_bit_cast(bf16x8_t,
-                                    __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-      }
-    };
-    read_frags(0, qf[0], pf[0]);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) read_frags(ks + 1, qf[(ks + 1) & 1], pf[(ks + 1) & 1]);
-      // keep the reads above ahead of this substep's MFMAs
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
-          acc[bj][bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks & 1][bj], pf[ks & 1][bi],
-                                                                acc[bj][bi], 0, 0, 0);
+    for (int m = 0; m < 16; ++m) {
+      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          F[0].q[m >> 2], F[0].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+      if (m < NR) issue_read(F[1], slot, 1, m);
       __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_stage_landed(kt + 1, min(kt + NSLOT - 2, nk - 1));
     __syncthreads();
-  }
+    settle(F[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int rslot = (kt + NSLOT - 1) % NSLOT, nslot = (kt + 1) % NSLOT;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          F[1].q[m >> 2], F[1].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+      // after MFMA m: DMA m/2 on even m, read m/2 on odd m, and reads
+      // 8..NR-1 after MFMAs 8..NR-1
+      if (REFILL && (m & 1) == 0) issue_dma(kt + NSLOT - 1, rslot, m >> 1);
+      if (NEXT && (m & 1) == 1) issue_read(F[0], nslot, 0, m >> 1);
+      if (NEXT && m >= 8 && m < NR) issue_read(F[0], nslot, 0, m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int kt = 0;
+  for (; kt + NSLOT - 1 < nk; ++kt) stage(kt, T_{}, T_{});
+  for (; kt + 1 < nk; ++kt) stage(kt, F_{}, T_{});
+  stage(kt, F_{}, F_{});
+  __syncthreads();
 
   // ---- epilogue.  Accumulator layout of the 32x32 MFMA (A operand = Q
   // rows j, B operand = P rows i): lane holds column i = lane%32 and rows
