@@ -73,12 +73,10 @@ hipError_t launch_adamw(void* params, int param_dtype, float* master, const void
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
-// round-to-nearest-even; NaN stays a (quiet) NaN
+// round-to-nearest-even, NaN stays NaN (gfx950 converts in hardware:
+// v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 }  // namespace muon

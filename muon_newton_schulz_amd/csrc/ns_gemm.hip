@@ -113,8 +113,11 @@ __device__ __forceinline__ void wait_frags(bf16x8_t* q, bf16x8_t* p) {
                : "memory");
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -307,65 +310,77 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
     mirror = ti != tj;
   }
 
+  // Staging-layout addressing.  For the accumulator positions of this
+  // lane, row il = bi*32 + frow has g(il) = g(frow), and the 8-byte slot
+  // of (il, bj*32 + 8q + 4*hl) is (bj*8 + 2q) ^ g(frow) ^ hl, so one base
+  // address per (bj, q) serves all four bi (+ bi * 8 KiB).  For the
+  // 16-byte row accesses (row r = lane/16 + 4u, chunk c = lane % 16) the
+  // chunk's two slots are (2c, 2c+1) ^ g(r) with g(r) = gr ^ (u & 7): one
+  // 16-byte access at the even slot, halves swapped when u is odd.
+  const int hl = lane >> 5;
+  const int gacc = (((frow & 3) << 3) | ((frow >> 2) & 7)) ^ hl;
+  const int gr = ((lane >> 4) & 3) << 3;
+  const int rc = lane & 15;
+  auto row_slot16 = [&](int u) {  // element offset of the 16-byte chunk
+    const int r = (lane >> 4) + 4 * u;
+    return r * 128 + (((2 * rc) ^ (gr | (u & 6))) << 2);
+  };
+
   if (PHASE == 2) {
     // b*A term: stage this wave's A sub-tile in LDS (16-byte row loads)
     const uint16_t* Ao = ws + md.ws_a;
 #pragma unroll 8
     for (int u = 0; u < 32; ++u) {
-      const int r = (lane >> 4) + 4 * u, c = lane & 15;
+      const int r = (lane >> 4) + 4 * u;
       u32x4_t v = *reinterpret_cast<const u32x4_t*>(Ao + static_cast<int64_t>(i0w + r) * ldc +
-                                                    j0w + 8 * c);
-      const int o0 = stg(r, 8 * c), o1 = stg(r, 8 * c + 4);
-      *reinterpret_cast<u32x2_t*>(S + o0) = u32x2_t{v[0], v[1]};
-      *reinterpret_cast<u32x2_t*>(S + o1) = u32x2_t{v[2], v[3]};
+                                                    j0w + 8 * rc);
+      if (u & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
+      *reinterpret_cast<u32x4_t*>(S + row_slot16(u)) = v;
     }
   }
-  __builtin_amdgcn_wave_barrier();
+  __syncthreads();
 
   // values -> LDS staging (8-byte slots)
   const float s2 = inv * inv;
-  const bool diag = ti == tj && PHASE != 3;
+  const bool diag = ti == tj && PHASE != 3 && (PHASE == 2 || g.c == 0.0f);
+  const float sc = PHASE == 1 ? (g.c != 0.0f ? 1.0f : g.b) * s2 : PHASE == 2 ? g.c : inv;
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+    for (int q = 0; q < 4; ++q) {
+      uint16_t* Sjq = S + frow * 128 + ((((bj * 8 + 2 * q) ^ gacc) & 31) << 2);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int il = bi * 32 + frow;
-        const int jl = bj * 32 + 8 * q + 4 * (lane >> 5);
-        const int o = stg(il, jl);
+      for (int bi = 0; bi < 4; ++bi) {
+        u32x2_t* slotp = reinterpret_cast<u32x2_t*>(Sjq + bi * 32 * 128);
         f32x4_t v;
-        if (PHASE == 1) {
-          const float bb = g.c != 0.0f ? 1.0f : g.b;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = bb * s2 * acc[bj][bi][4 * q + e];
-        } else if (PHASE == 2) {
-          const u32x2_t a0 = *reinterpret_cast<const u32x2_t*>(S + o);
-          const f32x4_t ao = {lo_bf(a0[0]), hi_bf(a0[0]), lo_bf(a0[1]), hi_bf(a0[1])};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = g.b * ao[e] + g.c * acc[bj][bi][4 * q + e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = inv * acc[bj][bi][4 * q + e];
+        for (int e = 0; e < 4; ++e) v[e] = sc * acc[bj][bi][4 * q + e];
+        if (PHASE == 2) {
+          const u32x2_t a0 = *slotp;
+          v[0] += g.b * lo_bf(a0[0]);
+          v[1] += g.b * hi_bf(a0[0]);
+          v[2] += g.b * lo_bf(a0[1]);
+          v[3] += g.b * hi_bf(a0[1]);
         }
-        if (diag && (PHASE == 2 || g.c == 0.0f)) {
+        if (diag) {
           // a on the diagonal of B
+          const int il = bi * 32 + frow, jl = bj * 32 + 8 * q + 4 * hl;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (i0w + il == j0w + jl + e) v[e] += g.a;
         }
-        *reinterpret_cast<u32x2_t*>(S + o) = u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])};
+        *slotp = u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])};
       }
-  __builtin_amdgcn_wave_barrier();
+    }
+  __syncthreads();
 
   // row stores: 16 bytes per lane, 4 rows of 256 bytes per instruction
 #pragma unroll 8
   for (int u = 0; u < 32; ++u) {
-    const int r = (lane >> 4) + 4 * u, c = lane & 15;
-    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(S + stg(r, 8 * c));
-    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(S + stg(r, 8 * c + 4));
-    *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(i0w + r) * ldc + j0w + 8 * c) =
-        u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    const int r = (lane >> 4) + 4 * u;
+    u32x4_t v = *reinterpret_cast<const u32x4_t*>(S + row_slot16(u));
+    if (u & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
+    *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(i0w + r) * ldc + j0w + 8 * rc) = v;
   }
 
   if (mirror) {
