@@ -25,6 +25,25 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ns_gemm_dense_d2048_l16_traffic.md")
+NS_SOURCE = os.path.join(ROOT, "muon_newton_schulz_amd", "csrc", "ns_gemm.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None when the summary is missing, is for
+    another workload, or was taken on a different kernel source."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(block)
+        sha = hashlib.sha256(open(NS_SOURCE, "rb").read()).hexdigest()
+    except (OSError, IndexError, ValueError):
+        return None
+    if data.get("ns_gemm_hip_sha256") != sha or data.get("workload") != workload:
+        return None
+    return data["fetch_bytes_per_launch"] + data["write_bytes_per_launch"]
 
 
 def parse():
@@ -237,7 +256,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": f3_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
+            "traffic_unit": "bytes per launch (HBM fetch + write, rocprofv3 counters scaled "
+                            "by a plain-copy calibration)",
             "flops_per_launch": f3,
             "avg_launch_ms": k["ns3"][0],
         },
