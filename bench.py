@@ -207,6 +207,20 @@ def main():
 
     k = {key: avg_ms(key) for key in ("momentum", "ns1", "ns2", "ns3", "apply", "adamw")}
 
+    # practical reference for the elementwise kernels: a plain device copy
+    # (read + write) of 1 GiB, outside the timed region
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b_ = ev(), ev()
+    a.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    b_.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * (1 << 30) / (a.elapsed_time(b_) * 1e-3) / 1e9
+    del src, dst
+
     # ---- algorithmic work
     shapes = wl.shapes
     mm = [(min(r, c), max(r, c)) for r, c in shapes]
@@ -282,6 +296,7 @@ def main():
             "apply": app_bytes / (k["apply"][0] * 1e-3) / 1e9,
             "adamw": sum(adam_bytes) / (adam_ms_total * 1e-3) / 1e9 if adam_ms_total else None,
             "peak": PEAK_HBM_GBPS,
+            "plain_copy_1GiB": copy_gbps,
         },
         "wall_s_timed_region": wall1 - wall0,
     }

@@ -12,7 +12,7 @@
 //                   section 3.1, decoupled decay; scale s per the K2
 //                   answer, sections 3.1 / 3.2).
 //  k_export         copies the current NS iterate out (stepwise checks).
-//  k_adamw          fused AdamW (optimizer tutorial, sections 2.3, 3.1,
+//  k_adamw_vec8     fused AdamW (optimizer tutorial, sections 2.3, 3.1,
 //                   3.3) with an optional fp32 master copy.
 //
 // All kernels are HBM-bound; accesses are coalesced along the contiguous
@@ -24,6 +24,11 @@ namespace muon {
 namespace {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -57,16 +62,49 @@ __device__ __forceinline__ NatDims nat_dims(const MatDev& md) {
   return d;
 }
 
+// 4 consecutive elements (bf16: 8 bytes, fp32: 16 bytes)
+template <typename T> struct V4;
+template <> struct V4<float> {
+  using type = float4;
+  static __device__ __forceinline__ f32x4v ld(const float* p, int64_t i) {
+    const float4 v = *reinterpret_cast<const float4*>(p + i);
+    return f32x4v{v.x, v.y, v.z, v.w};
+  }
+  static __device__ __forceinline__ void st(float* p, int64_t i, f32x4v v) {
+    *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct V4<uint16_t> {
+  static __device__ __forceinline__ f32x4v ld(const uint16_t* p, int64_t i) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p + i);
+    return f32x4v{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+  }
+  static __device__ __forceinline__ void st(uint16_t* p, int64_t i, f32x4v v) {
+    uint2 w;
+    w.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    w.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    *reinterpret_cast<uint2*>(p + i) = w;
+  }
+};
+
+// A matrix can use 4-wide accesses when its rows start on 4-element
+// boundaries of the flat buffers (the buffers themselves are checked on
+// the host).
+__device__ __forceinline__ bool vec4_ok(const MatDev& md, int bufs_aligned) {
+  return bufs_aligned && (md.off & 3) == 0 && (md.cols & 3) == 0;
+}
+
 // One 64x64 tile (natural coordinates) of one matrix per block, covering
 // the padded extent so the zero padding of the NS operand is (re)written
-// every step.
+// every step.  4-wide path: thread = 4 consecutive columns x 4 rows.
 template <typename GT, typename UT>
 __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mats,
                                                   const Item* __restrict__ items,
                                                   const GT* __restrict__ grads,
                                                   float* __restrict__ mom, UT* __restrict__ ws,
                                                   float* __restrict__ partials, float mu,
-                                                  int nesterov) {
+                                                  int nesterov, int bufs_aligned) {
   __shared__ float tile[kEwTile][kEwTile + 1];
   __shared__ float wsum[4];
   const Item it = items[blockIdx.x];
@@ -74,32 +112,69 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
   const int r0 = (it.rc >> 16) * kEwTile, c0 = (it.rc & 0xffff) * kEwTile;
   const NatDims nd = nat_dims(md);
   UT* X = ws + md.ws_x[0];
-  const int lc = threadIdx.x & 63, lr = threadIdx.x >> 6;
   const float omm = 1.0f - mu;
-  const int c = c0 + lc;
   float ss = 0.0f;
-#pragma unroll 4
-  for (int q = 0; q < 16; ++q) {
-    const int rr = lr + 4 * q, r = r0 + rr;
-    float u = 0.0f;
-    if (r < md.rows && c < md.cols) {
-      const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
-      const float g = Elem<GT>::ld(grads, e);
-      const float m = mu * mom[e] + omm * g;
-      mom[e] = m;
-      u = nesterov ? mu * m + omm * g : m;
+  if (vec4_ok(md, bufs_aligned)) {
+    const int cg = (threadIdx.x & 15) * 4, rg = threadIdx.x >> 4;
+    const int c = c0 + cg;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = rg + 16 * q, r = r0 + rr;
+      f32x4v u = {0.f, 0.f, 0.f, 0.f};
+      if (r < md.rows && c < md.cols) {
+        const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
+        const f32x4v g = V4<GT>::ld(grads, e);
+        f32x4v m = V4<float>::ld(mom, e);
+        m = mu * m + omm * g;
+        V4<float>::st(mom, e, m);
+        u = nesterov ? mu * m + omm * g : m;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ss = fmaf(u[k], u[k], ss);
+      if (md.trans) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tile[rr][cg + k] = u[k];
+      } else {
+        V4<UT>::st(X, static_cast<int64_t>(r) * nd.cp + c, u);
+      }
     }
-    ss = fmaf(u, u, ss);
-    if (md.trans) tile[rr][lc] = u;
-    else Elem<UT>::st(X, static_cast<int64_t>(r) * nd.cp + c, u);
-  }
-  if (md.trans) {
-    // X = U^T: X[c][r], coalesced along r
-    __syncthreads();
+    if (md.trans) {
+      // X = U^T: thread writes X[c][r..r+3] (4 consecutive rows of U)
+      __syncthreads();
+      const int rq = (threadIdx.x & 15) * 4, cc0 = threadIdx.x >> 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cc = cc0 + 16 * q;
+        const f32x4v v = {tile[rq][cc], tile[rq + 1][cc], tile[rq + 2][cc], tile[rq + 3][cc]};
+        V4<UT>::st(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + rq, v);
+      }
+    }
+  } else {
+    const int lc = threadIdx.x & 63, lr = threadIdx.x >> 6;
+    const int c = c0 + lc;
 #pragma unroll 4
     for (int q = 0; q < 16; ++q) {
-      const int cc = lr + 4 * q;
-      Elem<UT>::st(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + lc, tile[lc][cc]);
+      const int rr = lr + 4 * q, r = r0 + rr;
+      float u = 0.0f;
+      if (r < md.rows && c < md.cols) {
+        const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
+        const float g = Elem<GT>::ld(grads, e);
+        const float m = mu * mom[e] + omm * g;
+        mom[e] = m;
+        u = nesterov ? mu * m + omm * g : m;
+      }
+      ss = fmaf(u, u, ss);
+      if (md.trans) tile[rr][lc] = u;
+      else Elem<UT>::st(X, static_cast<int64_t>(r) * nd.cp + c, u);
+    }
+    if (md.trans) {
+      // X = U^T: X[c][r], coalesced along r
+      __syncthreads();
+#pragma unroll 4
+      for (int q = 0; q < 16; ++q) {
+        const int cc = lr + 4 * q;
+        Elem<UT>::st(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + lc, tile[lc][cc]);
+      }
     }
   }
   ss = wave_sum(ss);
@@ -171,15 +246,56 @@ __global__ __launch_bounds__(256) void k_apply(const MatDev* __restrict__ mats,
                                                PT* __restrict__ params, const UT* __restrict__ ws,
                                                const float* __restrict__ inv, int use_inv,
                                                int x_final, float lr, float wd, int scale_mode,
-                                               float rms_target, float* __restrict__ out_update) {
+                                               float rms_target, float* __restrict__ out_update,
+                                               int bufs_aligned) {
   __shared__ float tile[kEwTile][kEwTile + 1];
   const Item it = items[blockIdx.x];
   const MatDev md = mats[it.mat];
   const int r0 = (it.rc >> 16) * kEwTile, c0 = (it.rc & 0xffff) * kEwTile;
-  const f32x16_t o = load_nat_tile<UT>(md, ws + (x_final ? md.ws_x[1] : md.ws_x[0]), r0, c0, tile);
+  const UT* X = ws + (x_final ? md.ws_x[1] : md.ws_x[0]);
   const float osc = use_inv ? inv[md.widx] : 1.0f;
   const float decay = 1.0f - lr * wd;
   const float step = lr * update_scale(md.rows, md.cols, scale_mode, rms_target);
+  if (vec4_ok(md, bufs_aligned)) {
+    // thread = 4 consecutive columns x 4 rows (16 elements)
+    const NatDims nd = nat_dims(md);
+    const int cg = (threadIdx.x & 15) * 4, rg = threadIdx.x >> 4;
+    f32x4v o[4];
+    if (!md.trans) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = V4<UT>::ld(X, static_cast<int64_t>(r0 + rg + 16 * q) * nd.cp + c0 + cg);
+    } else {
+      // X[c][r]: 4 consecutive r per thread, transposed through LDS
+      const int rq = (threadIdx.x & 15) * 4, cc0 = threadIdx.x >> 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cc = cc0 + 16 * q;
+        const f32x4v v = V4<UT>::ld(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + rq);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tile[rq + k][cc] = v[k];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[q][k] = tile[rg + 16 * q][cg + k];
+    }
+    const int c = c0 + cg;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + rg + 16 * q;
+      if (r < md.rows && c < md.cols) {
+        const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
+        const f32x4v oo = o[q] * osc;
+        const f32x4v w = V4<PT>::ld(params, e);
+        V4<PT>::st(params, e, decay * w - step * oo);
+        if (out_update) V4<float>::st(out_update, e, oo);
+      }
+    }
+    return;
+  }
+  const f32x16_t o = load_nat_tile<UT>(md, X, r0, c0, tile);
   const int c = c0 + (threadIdx.x & 63);
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -246,71 +362,79 @@ __global__ __launch_bounds__(256) void k_adamw_scalar(PT* __restrict__ params,
                               decay);
 }
 
-template <typename T> struct Vec4;
-template <> struct Vec4<float> { using type = float4; };
-template <> struct Vec4<uint16_t> { using type = ushort4; };
+// 8 consecutive elements per thread and iteration: bf16 vectors are 16
+// bytes, fp32 vectors two 16-byte loads.  Every pointer is aligned to 8
+// elements (checked on the host); the tail of n % 8 elements is done by the
+// first threads of block 0.
+template <typename T>
+__device__ __forceinline__ void ld8(const T* p, int64_t q, float* o);
+template <>
+__device__ __forceinline__ void ld8<float>(const float* p, int64_t q, float* o) {
+  const float4 a = reinterpret_cast<const float4*>(p)[2 * q];
+  const float4 b = reinterpret_cast<const float4*>(p)[2 * q + 1];
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void ld8<uint16_t>(const uint16_t* p, int64_t q, float* o) {
+  const uint4 a = reinterpret_cast<const uint4*>(p)[q];
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(w[k] << 16);
+    o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st8(T* p, int64_t q, const float* o);
+template <>
+__device__ __forceinline__ void st8<float>(float* p, int64_t q, const float* o) {
+  reinterpret_cast<float4*>(p)[2 * q] = make_float4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<float4*>(p)[2 * q + 1] = make_float4(o[4], o[5], o[6], o[7]);
+}
+template <>
+__device__ __forceinline__ void st8<uint16_t>(uint16_t* p, int64_t q, const float* o) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = static_cast<uint32_t>(f32_to_bf16(o[2 * k])) |
+           (static_cast<uint32_t>(f32_to_bf16(o[2 * k + 1])) << 16);
+  reinterpret_cast<uint4*>(p)[q] = make_uint4(w[0], w[1], w[2], w[3]);
+}
 
-__device__ __forceinline__ void to_f4(const float4& a, float* o) {
-  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-}
-__device__ __forceinline__ void to_f4(const ushort4& a, float* o) {
-  o[0] = bf16_to_f32(a.x); o[1] = bf16_to_f32(a.y);
-  o[2] = bf16_to_f32(a.z); o[3] = bf16_to_f32(a.w);
-}
-__device__ __forceinline__ void from_f4(const float* o, float4& a) {
-  a.x = o[0]; a.y = o[1]; a.z = o[2]; a.w = o[3];
-}
-__device__ __forceinline__ void from_f4(const float* o, ushort4& a) {
-  a.x = f32_to_bf16(o[0]); a.y = f32_to_bf16(o[1]);
-  a.z = f32_to_bf16(o[2]); a.w = f32_to_bf16(o[3]);
-}
-
-// Vector variant: 4 elements per thread per iteration; every pointer is
-// aligned to 4 elements (checked on the host); the tail of n % 4 elements
-// is done by the first threads of block 0.
 template <typename PT, typename GT, bool MASTER>
-__global__ __launch_bounds__(256) void k_adamw_vec4(PT* __restrict__ params,
+__global__ __launch_bounds__(256) void k_adamw_vec8(PT* __restrict__ params,
                                                     float* __restrict__ master,
                                                     const GT* __restrict__ grads,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     int64_t n, float b1, float b2, float eps,
                                                     float lr_bc1, float rsqrt_bc2, float decay) {
-  using PV = typename Vec4<PT>::type;
-  using GV = typename Vec4<GT>::type;
-  const int64_t n4 = n >> 2;
+  const int64_t n8 = n >> 3;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < n4;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < n8;
        q += stride) {
-    float g[4], th[4], mm[4], vv[4];
-    to_f4(reinterpret_cast<const GV*>(grads)[q], g);
-    if (MASTER) to_f4(reinterpret_cast<const float4*>(master)[q], th);
-    else to_f4(reinterpret_cast<const PV*>(params)[q], th);
-    to_f4(reinterpret_cast<const float4*>(m)[q], mm);
-    to_f4(reinterpret_cast<const float4*>(v)[q], vv);
+    float g[8], th[8], mm[8], vv[8];
+    ld8<GT>(grads, q, g);
+    if (MASTER) ld8<float>(master, q, th);
+    else ld8<PT>(params, q, th);
+    ld8<float>(m, q, mm);
+    ld8<float>(v, q, vv);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 8; ++k) {
       mm[k] = b1 * mm[k] + (1.0f - b1) * g[k];
       vv[k] = b2 * vv[k] + (1.0f - b2) * g[k] * g[k];
       const float den = sqrtf(vv[k]) * rsqrt_bc2 + eps;
       th[k] = th[k] * decay - lr_bc1 * (mm[k] / den);
     }
-    float4 o;
-    from_f4(mm, o); reinterpret_cast<float4*>(m)[q] = o;
-    from_f4(vv, o); reinterpret_cast<float4*>(v)[q] = o;
-    if (MASTER) { from_f4(th, o); reinterpret_cast<float4*>(master)[q] = o; }
-    PV pv;
-    from_f4(th, pv);
-    reinterpret_cast<PV*>(params)[q] = pv;
+    st8<float>(m, q, mm);
+    st8<float>(v, q, vv);
+    if (MASTER) st8<float>(master, q, th);
+    st8<PT>(params, q, th);
   }
-  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
-    const int64_t i = (n4 << 2) + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const int64_t i = (n8 << 3) + threadIdx.x;
     adamw_one<PT, GT, MASTER>(params, master, grads, m, v, i, b1, b2, eps, lr_bc1, rsqrt_bc2,
                               decay);
   }
-}
-
-inline bool aligned(const void* p, size_t a) {
-  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
 template <typename PT, typename GT, bool MASTER>
@@ -319,14 +443,14 @@ hipError_t adamw_dispatch(void* params, float* master, const void* grads, float*
                           float rsqrt_bc2, float decay, hipStream_t s) {
   PT* p = static_cast<PT*>(params);
   const GT* g = static_cast<const GT*>(grads);
-  const bool vec = aligned(p, 4 * sizeof(PT)) && aligned(g, 4 * sizeof(GT)) &&
-                   aligned(m, 16) && aligned(v, 16) && (!MASTER || aligned(master, 16));
-  const int64_t work = vec ? (n >> 2) : n;
+  const bool vec = aligned(p, 8 * sizeof(PT)) && aligned(g, 8 * sizeof(GT)) &&
+                   aligned(m, 32) && aligned(v, 32) && (!MASTER || aligned(master, 32));
+  const int64_t work = vec ? (n >> 3) : n;
   int64_t blocks = (work + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   if (vec)
-    hipLaunchKernelGGL((k_adamw_vec4<PT, GT, MASTER>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((k_adamw_vec8<PT, GT, MASTER>), dim3(static_cast<unsigned>(blocks)),
                        dim3(256), 0, s, p, master, g, m, v, n, b1, b2, eps, lr_bc1, rsqrt_bc2,
                        decay);
   else
@@ -345,10 +469,11 @@ hipError_t launch_momentum(const MatDev* mats, const Item* items, int n_items, i
                            float* partials, float mu, int nesterov, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items), block(256);
+  const int al = aligned(grads, 4 * (grad_dtype == 1 ? 2 : 4)) && aligned(mom, 16);
 #define MUON_K1(GT, UT)                                                                   \
   hipLaunchKernelGGL((k_momentum<GT, UT>), grid, block, 0, s, mats, items,                \
                      static_cast<const GT*>(grads), mom, static_cast<UT*>(ws), partials, mu, \
-                     nesterov)
+                     nesterov, al)
   if (grad_dtype == 1 && ns_dtype == 1) MUON_K1(uint16_t, uint16_t);
   else if (grad_dtype == 1 && ns_dtype == 0) MUON_K1(uint16_t, float);
   else if (grad_dtype == 0 && ns_dtype == 1) MUON_K1(float, uint16_t);
@@ -373,10 +498,12 @@ hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int 
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items), block(256);
   const int use_inv = o_scale_by_inv != 0.0f;
+  const int al = aligned(params, 4 * (param_dtype == 1 ? 2 : 4)) &&
+                 (out_update == nullptr || aligned(out_update, 16));
 #define MUON_K7(PT, UT)                                                                       \
   hipLaunchKernelGGL((k_apply<PT, UT>), grid, block, 0, s, mats, items, static_cast<PT*>(params), \
                      static_cast<const UT*>(ws), inv, use_inv, x_final, lr, wd, scale_mode,     \
-                     rms_target, out_update)
+                     rms_target, out_update, al)
   if (param_dtype == 1 && ns_dtype == 1) MUON_K7(uint16_t, uint16_t);
   else if (param_dtype == 1 && ns_dtype == 0) MUON_K7(uint16_t, float);
   else if (param_dtype == 0 && ns_dtype == 1) MUON_K7(float, uint16_t);

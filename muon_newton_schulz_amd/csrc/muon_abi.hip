@@ -47,6 +47,7 @@ struct Wave {
 
 struct muon_plan {
   int device = 0;
+  int n_cu = 256;  // compute units of the plan's device (persistent grid size)
   int32_t n_mats = 0;
   int64_t flat_numel = 0;
   int32_t param_dtype = 0, grad_dtype = 0, ns_dtype = 0;
@@ -282,6 +283,10 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
 int upload_plan(muon_plan& p) {
   hipError_t e = hipGetDevice(&p.device);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&p.n_cu, hipDeviceAttributeMultiprocessorCount, p.device);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+  // the XCD-grouped tile order assumes a grid that is a multiple of the XCD count
+  p.n_cu = p.n_cu >= 8 ? p.n_cu / 8 * 8 : p.n_cu;
   const size_t b_mats = align_up(p.mats.size() * sizeof(MatDev), kAlign);
   const size_t b_k1 = align_up(p.k1_items.size() * sizeof(Item), kAlign);
   const size_t b_syrk = align_up(p.syrk_items.size() * sizeof(Item), kAlign);
@@ -473,8 +478,9 @@ int muon_stage_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
   const Wave& w = plan->waves[wave];
   const Item* items = phase == 3 ? plan->d_bx + w.bx_begin : plan->d_syrk + w.syrk_begin;
   const int n = static_cast<int>(phase == 3 ? w.bx_count : w.syrk_count);
-  const muon::GemmArgs g = gemm_args(plan, w, workspace, hp, iter, items);
-  const hipError_t e = muon::launch_ns_phase(plan->ns_dtype, phase, n, g, stream);
+  muon::GemmArgs g = gemm_args(plan, w, workspace, hp, iter, items);
+  g.n_items = n;
+  const hipError_t e = muon::launch_ns_phase(plan->ns_dtype, phase, n, plan->n_cu, g, stream);
   if (e != hipSuccess) return hip_fail(e, "NS kernel launch");
   return MUON_OK;
 }

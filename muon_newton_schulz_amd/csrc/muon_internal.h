@@ -45,6 +45,7 @@ struct GemmArgs {
   float a, b, c;
   int32_t first;      // first NS iteration: fold the normalisation in
   int32_t x_cur;      // X buffer read by phases 1 and 3 (phase 3 writes 1 - x_cur)
+  int32_t n_items;    // tile-list length (the persistent grid walks it)
 };
 
 // kernel launchers (defined in the .hip files)
@@ -62,8 +63,8 @@ hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int 
                         hipStream_t s);
 hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int ns_dtype,
                          const void* ws, int x_idx, float* out, hipStream_t s);
-hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, const GemmArgs& args,
-                           hipStream_t s);
+hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
+                           const GemmArgs& args, hipStream_t s);
 hipError_t launch_adamw(void* params, int param_dtype, float* master, const void* grads,
                         int grad_dtype, float* m, float* v, int64_t n, float lr,
                         float beta1, float beta2, float eps, float wd, float lr_bc1,

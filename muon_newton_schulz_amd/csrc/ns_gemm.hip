@@ -129,11 +129,9 @@ __device__ __forceinline__ int stg(int i, int j) {
   return i * 128 + ((((j >> 2) ^ g) & 31) << 2);
 }
 
+// One 256x256 output tile: operand pipeline, MFMA main loop, epilogue.
 template <int PHASE>
-__global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * 2 * BT * BK];  // 128 KiB
-  const Item it = g.items[blockIdx.x];
-  if (it.mat < 0) return;  // padding of the XCD-grouped dispatch order
+__device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16_t* smem) {
   const MatDev md = g.mats[it.mat];
   const int ti = it.rc >> 16, tj = it.rc & 0xffff;
   uint16_t* ws = static_cast<uint16_t*>(g.ws);
@@ -403,6 +401,24 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
   }
 }
 
+// Persistent launch: one workgroup per CU walks the tile list with stride
+// gridDim.x.  The list is in XCD-grouped order for a grid that is a
+// multiple of 8, so the 32 workgroups of an XCD still work on one group of
+// neighbouring tiles at a time; a tile's epilogue stores drain while the
+// next tile's first operand stages load.
+template <int PHASE>
+__global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * 2 * BT * BK];  // 128 KiB
+  bool busy = false;
+  for (int idx = blockIdx.x; idx < g.n_items; idx += gridDim.x) {
+    const Item it = g.items[idx];
+    if (it.mat < 0) continue;  // padding of the XCD-grouped order
+    if (busy) __syncthreads();  // the previous tile's epilogue is done with LDS
+    busy = true;
+    ns_tile<PHASE>(g, it, smem);
+  }
+}
+
 // ------------------------------------------------------------ fp32 engine
 
 constexpr int FT = kTileFp32;  // 64
@@ -413,7 +429,7 @@ __global__ __launch_bounds__(256) void k_ns_f32(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float Ps[FK][FT + 4];
   __shared__ __attribute__((aligned(16))) float Qs[FK][FT + 4];
   const Item it = g.items[blockIdx.x];
-  if (it.mat < 0) return;  // padding of the XCD-grouped dispatch order
+  if (it.mat < 0) return;  // padding of the XCD-grouped order
   const MatDev md = g.mats[it.mat];
   const int ti = it.rc >> 16, tj = it.rc & 0xffff;
   float* ws = static_cast<float*>(g.ws);
@@ -505,15 +521,17 @@ __global__ __launch_bounds__(256) void k_ns_f32(GemmArgs g) {
 
 }  // namespace
 
-hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, const GemmArgs& args,
-                           hipStream_t s) {
+hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
+                           const GemmArgs& args, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
-  const dim3 grid(n_items), block(256);
+  const dim3 block(256);
   if (ns_dtype == 1) {
+    const dim3 grid(n_items < n_cu ? n_items : n_cu);
     if (phase == 1) hipLaunchKernelGGL(k_ns_bf16<1>, grid, block, 0, s, args);
     else if (phase == 2) hipLaunchKernelGGL(k_ns_bf16<2>, grid, block, 0, s, args);
     else hipLaunchKernelGGL(k_ns_bf16<3>, grid, block, 0, s, args);
   } else {
+    const dim3 grid(n_items);
     if (phase == 1) hipLaunchKernelGGL(k_ns_f32<1>, grid, block, 0, s, args);
     else if (phase == 2) hipLaunchKernelGGL(k_ns_f32<2>, grid, block, 0, s, args);
     else hipLaunchKernelGGL(k_ns_f32<3>, grid, block, 0, s, args);

@@ -167,7 +167,7 @@ def test_adamw_bf16_master_dense_groups_sampled(gpu):
             assert np.all(np.abs(np64(a.param[s]) - pr) <= ulp * 1.01)
 
 
-@pytest.mark.parametrize("n,off", [(1001, 1), (3, 0), (4099, 3), (1, 0)])
+@pytest.mark.parametrize("n,off", [(1001, 1), (3, 0), (4099, 3), (1, 0), (1001, 0), (4101, 8)])
 def test_adamw_unaligned_and_tails(gpu, n, off):
     g_ = torch.Generator(device=gpu)
     g_.manual_seed(n + off)
@@ -230,6 +230,19 @@ def _flat(shapes, gap=3):
 def test_muon_ragged_edge_shapes(gpu, ns_dtype, pdt):
     mats, n = _flat(EDGE_SHAPES)
     s = Setup(mats, n, pdt, pdt, ns_dtype, gpu, seed=3)
+    check_muon_step(s, mhp(QUINTIC), tol_w=1e-2 if pdt == "bf16" else 1e-4)
+
+
+# row starts on 4-element boundaries: the 4-wide momentum / apply paths,
+# tall and wide, with rows off the 64-row tile grid
+ALIGNED_SHAPES = [(36, 100), (100, 36), (130, 516), (516, 132), (4, 8), (8, 4), (64, 64)]
+
+
+@pytest.mark.parametrize("ns_dtype,pdt", [("bf16", "bf16"), ("fp32", "fp32")])
+def test_muon_vector_paths_aligned_ragged(gpu, ns_dtype, pdt):
+    mats, n = _flat(ALIGNED_SHAPES, gap=4)
+    assert all(o % 4 == 0 and c % 4 == 0 for o, r, c in mats)
+    s = Setup(mats, n, pdt, pdt, ns_dtype, gpu, seed=4)
     check_muon_step(s, mhp(QUINTIC), tol_w=1e-2 if pdt == "bf16" else 1e-4)
 
 
@@ -395,8 +408,10 @@ def test_empty_plan_and_bad_workspace(gpu):
 # ---------------------------------------------------------------- full-size workloads
 
 
-def _workload_sampled(gpu, name, sample, hp, cap=0):
+def _workload_sampled(gpu, name, sample, hp, cap=0, first=None):
     wl = W.workload(name)
+    if first is not None:  # the first `first` matrices of the workload, at full size
+        wl.shapes = wl.shapes[:first]
     inp = W.make_muon_inputs(wl, gpu, step=1)
     plan = M.muon_plan_create(wl.mats(), wl.muon_numel(), wl.param_dtype, wl.grad_dtype,
                               "bf16", cap)
@@ -427,3 +442,39 @@ def test_dense_stack_full_size_sampled(gpu):
 
 def test_moe_e64_full_size_sampled(gpu):
     _workload_sampled(gpu, "moe_e64_2048x1408", [0, 127, 150], mhp(QUINTIC))
+
+
+def test_moe_e384_shapes_sampled(gpu):
+    # 8 experts x (gate, up 7168x2048; down 2048x7168): the large expert
+    # shapes of the 384-expert workload; matrices 0 (gate), 8 (up) and 16
+    # (down, tall)
+    wl = W.workload("moe_e384_7168x2048")
+    shapes = wl.shapes[:8] + wl.shapes[384:392] + wl.shapes[768:776]
+    assert shapes[0] == (7168, 2048) and shapes[16] == (2048, 7168)
+    wl.shapes = shapes
+    inp = W.make_muon_inputs(wl, gpu, step=1)
+    hp = mhp(QUINTIC)
+    plan = M.muon_plan_create(wl.mats(), wl.muon_numel(), "bf16", "bf16", "bf16")
+    ws = plan.alloc_workspace(gpu)
+    out = torch.zeros(wl.muon_numel(), device=gpu)
+    mats = wl.mats()
+    before = {i: tuple(np64(t[o:o + r * c]) for t in (inp.params, inp.grads, inp.momentum))
+              for i, (o, r, c) in ((i, mats[i]) for i in (0, 16))}
+    M.muon_step(plan, inp.params, inp.grads, inp.momentum, ws, hp, out)
+    torch.cuda.synchronize()
+    for i in (0, 16):
+        o, r, c = mats[i]
+        Wn, Mn, On = O.muon_matrix_math(*(x.reshape(r, c) for x in before[i]), ohp(hp))
+        assert rel(np64(out[o:o + r * c]).reshape(r, c), On) <= 1e-2, i
+        assert rel(np64(inp.momentum[o:o + r * c]), O.fp32_round(Mn).ravel()) <= 2e-6
+
+
+def test_ragged_shapes_full_size_sampled(gpu):
+    # the first 40 shapes of the seeded ragged draw (square / tall / wide,
+    # every tenth off the 64 grid), oracle on four of them including two
+    # off-grid matrices
+    wl = W.workload("ragged_500")
+    shapes = wl.shapes[:40]
+    small = sorted(range(40), key=lambda i: min(shapes[i]))
+    sample = sorted(set([i for i in small if i % 10 == 0][:2] + small[:2]))
+    _workload_sampled(gpu, "ragged_500", sample, mhp(QUINTIC), first=40)
