@@ -60,9 +60,17 @@ constexpr int BK = 32;           // K per pipeline stage
 constexpr int NSLOT = 4;         // LDS ring slots (stages in flight: NSLOT - 1)
 constexpr int DMA_PER_STAGE = 8;  // DMA instructions per wave per stage
 
-// 16 bytes per lane, HBM -> LDS; lane l's data lands at lds + 16*l.
-__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_wave_uniform) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)lds_wave_uniform, 16, 0, 0);
+// 16 bytes per lane, HBM -> LDS; lane l's data lands at lds + 16*l.  The
+// source is a wave-uniform base plus a 32-bit per-lane byte offset, the
+// instruction's SGPR-base + VGPR-offset form: advancing a stage is scalar
+// arithmetic only.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint16_t* lds_wave_uniform) {
+  // one opaque 64-bit scalar, so that the address is matched as
+  // SGPR base + zero-extended VGPR offset
+  uint64_t sbase = reinterpret_cast<uint64_t>(base);
+  asm("" : "+s"(sbase));
+  __builtin_amdgcn_global_load_lds((gbl_void_t)(reinterpret_cast<const char*>(sbase) + voff),
+                                   (lds_void_t)lds_wave_uniform, 16, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -76,18 +84,34 @@ __device__ __forceinline__ s16x4_t ld_tr(const uint16_t* p) {
 }
 
 // Main-loop fragment reads are issued as inline asm: the compiler's
-// wait-count pass would otherwise make every transpose read wait for all
-// LDS DMA in flight (vmcnt(0)), which drains the load pipeline.  Their
-// completion is awaited explicitly with wait_frags before use.
-__device__ __forceinline__ s16x4_t ld_tr_async(const uint16_t* p) {
+// wait-count pass would otherwise make every LDS read wait for all LDS DMA
+// in flight (vmcnt(0)), which drains the load pipeline.  Their completion
+// is awaited explicitly with wait_frags before use.  OFF is the
+// instruction's immediate byte offset.
+template <int OFF>
+__device__ __forceinline__ s16x4_t ld_tr_async(uint32_t addr) {
   s16x4_t r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)) : "memory");
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
   return r;
 }
-__device__ __forceinline__ bf16x8_t ld128_async(const uint16_t* p) {
+template <int OFF>
+__device__ __forceinline__ bf16x8_t ld128_async(uint32_t addr) {
   u32x4_t r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)) : "memory");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
   return __builtin_bit_cast(bf16x8_t, r);
+}
+
+template <int N>
+using Int = std::integral_constant<int, N>;
+
+// f(Int<I>{}), ..., f(Int<N-1>{}): loop bodies that need the index as a
+// compile-time constant (immediate offsets, register-array indices).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 // Wait until this wave's DMA for stage `st` has landed, given that stages
 // up to `newest` have been issued (DMA_PER_STAGE instructions each); the
@@ -102,6 +126,14 @@ __device__ __forceinline__ void wait_stage_landed(int st, int newest) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Bare workgroup barrier for the operand pipeline.  A fenced barrier
+// (__syncthreads) makes the compiler wait for every vector memory
+// instruction in flight first (vmcnt(0)), LDS DMA included, which would
+// drain the pipeline.  Here nothing else is needed: each wave has waited
+// for its own DMA of the stage (wait_stage_landed) and for its own
+// fragment reads (wait_frags) before it arrives.
+__device__ __forceinline__ void pipe_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Wait until at most N LDS reads are outstanding; the fragments are tied
 // to the wait so that their consumers cannot be scheduled above it.
 template <int N>
@@ -109,6 +141,17 @@ __device__ __forceinline__ void wait_frags(bf16x8_t* q, bf16x8_t* p) {
   asm volatile("s_waitcnt lgkmcnt(%8)"
                : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(p[0]), "+v"(p[1]),
                  "+v"(p[2]), "+v"(p[3])
+               : "n"(N)
+               : "memory");
+}
+
+// Same for the transposed halves of phase 3 (the Q fragments are
+// assembled from them only after the wait).
+template <int N>
+__device__ __forceinline__ void wait_frags_tr(s16x4_t* t, bf16x8_t* p) {
+  asm volatile("s_waitcnt lgkmcnt(%12)"
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]),
+                 "+v"(t[6]), "+v"(t[7]), "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3])
                : "n"(N)
                : "memory");
 }
@@ -122,6 +165,12 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// The lane id, hidden from the optimiser (see the epilogue).
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
 // staging layout of a wave's 128x128 bf16 result: element offset of the
 // 4-element (8-byte) slot holding (i, j..j+3), j % 4 == 0
 __device__ __forceinline__ int stg(int i, int j) {
@@ -131,9 +180,8 @@ __device__ __forceinline__ int stg(int i, int j) {
 
 // One 256x256 output tile: operand pipeline, MFMA main loop, epilogue.
 template <int PHASE>
-__device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16_t* smem) {
-  const MatDev md = g.mats[it.mat];
-  const int ti = it.rc >> 16, tj = it.rc & 0xffff;
+__device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, const int ti,
+                                        const int tj, const float inv, uint16_t* smem) {
   uint16_t* ws = static_cast<uint16_t*>(g.ws);
 
   // operands
@@ -162,38 +210,58 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
   // MFMA operand fragments.  A fragment set (one 16-wide k substep) is
   // NR LDS reads: 4 P fragments (ds_read_b128) then the Q fragments, 4
   // ds_read_b128 (phases 1, 2) or 8 transpose reads (phase 3, lo/hi halves
-  // of 8 consecutive k).  Read r of a set is issued by issue_read so that
-  // the reads can be interleaved one by one with MFMAs.
+  // of 8 consecutive k).  Read R of a set is issued by issue_read so that
+  // the reads can be interleaved one by one with MFMAs.  Addresses: a
+  // per-lane byte offset within a ring slot (below) + the wave-uniform slot
+  // base + an immediate.
   constexpr int NR = PHASE == 3 ? 12 : 8;
+  constexpr uint32_t SLOT_BYTES = 2 * BT * BK * 2;
+  const uint32_t lds0 = lds_addr(smem);
+  uint32_t vp[2], vq[2];  // K-contiguous fragments of k substep ks
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int sw = ((ks * 2 + (lane >> 5)) ^ ((frow >> 2) & 3)) << 3;
+    vp[ks] = ((wi * 128 + frow) * BK + sw) * 2;
+    vq[ks] = BT * BK * 2 + ((wj * 128 + frow) * BK + sw) * 2;
+  }
+  // phase 3: transposed reads of column block b.  Lane group of 16: k row
+  // 8*(lane/32) + (lane%16)/4 (+4 for the hi half, +16 per substep), columns
+  // wj*128 + 32b + 16*((lane/16)%2) + 4*(lane%4), whose 32-column block is
+  // swizzled by (k & 3) = (lane%16)/4.
+  uint32_t vt[4];
+  {
+    const int s = lane & 15, yy = (s >> 2) & 3;
+    const int x = 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      vt[b] = BT * BK * 2 + ((8 * (lane >> 5) + (s >> 2)) * BT + wj * 128 + x + ((b ^ yy) << 5)) * 2;
+  }
   struct Frags {
     bf16x8_t p[4];
     bf16x8_t q[4];
     s16x4_t t[8];  // phase 3: transposed halves of q
   };
-  auto issue_read = [&](Frags& f, int slot, int ks, int r) {
-    const uint16_t* sp = smem + slot * 2 * BT * BK;
-    const uint16_t* sq = sp + BT * BK;
-    if (r < 4 || PHASE != 3) {
-      const int kc = ks * 2 + (lane >> 5);
-      const int sw = (kc ^ ((frow >> 2) & 3)) << 3;
-      if (r < 4) f.p[r] = ld128_async(sp + (wi * 128 + r * 32 + frow) * BK + sw);
-      else f.q[r - 4] = ld128_async(sq + (wj * 128 + (r - 4) * 32 + frow) * BK + sw);
+  auto issue_read = [&](Frags& f, uint32_t sb, auto ks_c, auto r_c) {
+    constexpr int KS = decltype(ks_c)::value, R = decltype(r_c)::value;
+    if constexpr (R < 4) {
+      f.p[R] = ld128_async<R * 32 * BK * 2>(vp[KS] + sb);
+    } else if constexpr (PHASE != 3) {
+      f.q[R - 4] = ld128_async<(R - 4) * 32 * BK * 2>(vq[KS] + sb);
     } else {
-      const int b = (r - 4) >> 1, h = (r - 4) & 1;
-      const int s = lane & 15;
-      const int kr = ks * 16 + 8 * (lane >> 5) + (s >> 2) + 4 * h;
-      const int col = (wj * 128 + b * 32 + 16 * ((lane >> 4) & 1) + 4 * (s & 3)) ^ ((kr & 3) << 5);
-      f.t[r - 4] = ld_tr_async(sq + kr * BT + col);
+      constexpr int B = (R - 4) >> 1, H = (R - 4) & 1;
+      f.t[R - 4] = ld_tr_async<KS * 16 * BT * 2 + H * 4 * BT * 2>(vt[B] + sb);
     }
   };
   // all reads of a set have landed (no other LDS reads outstanding)
   auto settle = [&](Frags& f) {
-    wait_frags<0>(f.q, f.p);
-    if (PHASE == 3) {
+    if constexpr (PHASE == 3) {
+      wait_frags_tr<0>(f.t, f.p);
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         f.q[b] = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(f.t[2 * b], f.t[2 * b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      wait_frags<0>(f.q, f.p);
     }
   };
 
@@ -205,24 +273,34 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  // DMA of one stage, one instruction at a time: instruction d (0..7) of
-  // this wave; d < 4: P rows, d >= 4: Q rows.
-  auto issue_dma = [&](int kt, int slot, int d) {
+  // DMA of one stage, one instruction at a time: instruction D (0..7) of
+  // this wave; D < 4: 16 P rows of 64 bytes (16-byte chunk c of row r at
+  // position c ^ ((r >> 2) & 3)), D >= 4: the same for Q (phases 1, 2) or
+  // 2 k-rows of 512 bytes of Q (phase 3, 32-column block q of k-row r at
+  // q ^ (r & 3)).  The per-lane source offsets are fixed for the tile.
+  const char* Pc = reinterpret_cast<const char*>(P);
+  const char* Qc = reinterpret_cast<const char*>(Q);
+  const int pc = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t dP = ((lane >> 2) * ldp + 8 * pc) * 2;
+  const uint32_t dQ = ((lane >> 2) * ldq + 8 * pc) * 2;
+  uint32_t dQ3[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    dQ3[par] = ((lane >> 5) * ldq + 8 * ((lane & 31) ^ (((2 * par + (lane >> 5)) & 3) << 2))) * 2;
+  auto issue_dma = [&](int kt, int slot, auto d_c) {
+    constexpr int D = decltype(d_c)::value, U = D & 3;
     uint16_t* sp = smem + slot * 2 * BT * BK;
     uint16_t* sq = sp + BT * BK;
-    const int k0 = kt * BK;
-    const int u = d & 3;
-    if (d < 4 || PHASE != 3) {
-      const int R0 = (wave * 4 + u) * 16;  // 16 rows of 64 bytes
-      const int row = R0 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
-      if (d < 4) dma16(P + static_cast<int64_t>(row) * ldp + k0 + 8 * c, sp + R0 * BK);
-      else dma16(Q + static_cast<int64_t>(row) * ldq + k0 + 8 * c, sq + R0 * BK);
+    const int64_t k0 = static_cast<int64_t>(kt) * BK;
+    if constexpr (D < 4) {
+      const int R0 = (wave * 4 + U) * 16;
+      dma16(Pc + (static_cast<int64_t>(R0) * ldp + k0) * 2, dP, sp + R0 * BK);
+    } else if constexpr (PHASE != 3) {
+      const int R0 = (wave * 4 + U) * 16;
+      dma16(Qc + (static_cast<int64_t>(R0) * ldq + k0) * 2, dQ, sq + R0 * BK);
     } else {
-      const int R0 = (wave * 4 + u) * 2;  // 2 k-rows of 512 bytes
-      const int row = R0 + (lane >> 5);
-      const int c = (lane & 31) ^ ((row & 3) << 2);
-      dma16(Q + static_cast<int64_t>(k0 + row) * ldq + 8 * c, sq + R0 * BT);
+      const int R0 = (wave * 4 + U) * 2;
+      dma16(Qc + (k0 + R0) * static_cast<int64_t>(ldq) * 2, dQ3[U & 1], sq + R0 * BT);
     }
   };
 
@@ -238,46 +316,45 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
   const int nk = K / BK;
 #pragma unroll
   for (int s0 = 0; s0 < NSLOT - 1; ++s0)
-    if (s0 < nk)
-      for (int d = 0; d < DMA_PER_STAGE; ++d) issue_dma(s0, s0, d);
+    if (s0 < nk) static_for<0, DMA_PER_STAGE>([&](auto d) { issue_dma(s0, s0, d); });
   wait_stage_landed(0, min(NSLOT - 2, nk - 1));
-  __syncthreads();
+  pipe_barrier();
 
   Frags F[2];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) issue_read(F[0], 0, 0, r);
+  static_for<0, NR>([&](auto r) { issue_read(F[0], lds0, Int<0>{}, r); });
 
   // one stage; REFILL: issue the DMA of stage kt+NSLOT-1, NEXT: read the
   // first fragments of stage kt+1 (both true except in the last stages)
   auto stage = [&](int kt, auto refill_c, auto next_c) {
     constexpr bool REFILL = decltype(refill_c)::value;
     constexpr bool NEXT = decltype(next_c)::value;
-    const int slot = kt % NSLOT;
+    const uint32_t sb = lds0 + (kt % NSLOT) * SLOT_BYTES;
     settle(F[0]);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    static_for<0, 16>([&](auto m_c) {
+      constexpr int m = decltype(m_c)::value;
       acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           F[0].q[m >> 2], F[0].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
-      if (m < NR) issue_read(F[1], slot, 1, m);
+      if constexpr (m < NR) issue_read(F[1], sb, Int<1>{}, Int<m>{});
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     wait_stage_landed(kt + 1, min(kt + NSLOT - 2, nk - 1));
-    __syncthreads();
+    pipe_barrier();
     settle(F[1]);
     __builtin_amdgcn_sched_barrier(0);
-    const int rslot = (kt + NSLOT - 1) % NSLOT, nslot = (kt + 1) % NSLOT;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    const int rslot = (kt + NSLOT - 1) % NSLOT;
+    const uint32_t nsb = lds0 + ((kt + 1) % NSLOT) * SLOT_BYTES;
+    static_for<0, 16>([&](auto m_c) {
+      constexpr int m = decltype(m_c)::value;
       acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           F[1].q[m >> 2], F[1].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
       // after MFMA m: DMA m/2 on even m, read m/2 on odd m, and reads
       // 8..NR-1 after MFMAs 8..NR-1
-      if (REFILL && (m & 1) == 0) issue_dma(kt + NSLOT - 1, rslot, m >> 1);
-      if (NEXT && (m & 1) == 1) issue_read(F[0], nslot, 0, m >> 1);
-      if (NEXT && m >= 8 && m < NR) issue_read(F[0], nslot, 0, m);
+      if constexpr (REFILL && (m & 1) == 0) issue_dma(kt + NSLOT - 1, rslot, Int<(m >> 1)>{});
+      if constexpr (NEXT && (m & 1) == 1) issue_read(F[0], nsb, Int<0>{}, Int<(m >> 1)>{});
+      if constexpr (NEXT && m >= 8 && m < NR) issue_read(F[0], nsb, Int<0>{}, Int<m>{});
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -292,9 +369,13 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
   // j = 8*(v/4) + 4*(lane/32) + v%4, i.e. C[i][j..j+3] for each v/4.
   // Wave sub-tile: rows i0w..i0w+127, columns j0w..j0w+127; LDS region of
   // this wave: 32 KiB (the operand buffers are no longer needed).
+  // The epilogue's lane-dependent addresses are derived from an opaque
+  // copy of the lane id, so the compiler cannot hoist them out of the
+  // persistent tile loop, where they would stay live across the main loop
+  // (and spill).
+  const int elane = opaque_lane(lane);
   uint16_t* S = smem + wave * (128 * 128);
   const int i0w = ti * BT + wi * 128, j0w = tj * BT + wj * 128;
-  const float inv = g.first ? g.inv[md.widx] : 1.0f;
   uint16_t* C;
   int ldc;
   bool mirror;
@@ -315,12 +396,13 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
   // 16-byte row accesses (row r = lane/16 + 4u, chunk c = lane % 16) the
   // chunk's two slots are (2c, 2c+1) ^ g(r) with g(r) = gr ^ (u & 7): one
   // 16-byte access at the even slot, halves swapped when u is odd.
-  const int hl = lane >> 5;
-  const int gacc = (((frow & 3) << 3) | ((frow >> 2) & 7)) ^ hl;
-  const int gr = ((lane >> 4) & 3) << 3;
-  const int rc = lane & 15;
+  const int efrow = elane & 31;
+  const int hl = elane >> 5;
+  const int gacc = (((efrow & 3) << 3) | ((efrow >> 2) & 7)) ^ hl;
+  const int gr = ((elane >> 4) & 3) << 3;
+  const int rc = elane & 15;
   auto row_slot16 = [&](int u) {  // element offset of the 16-byte chunk
-    const int r = (lane >> 4) + 4 * u;
+    const int r = (elane >> 4) + 4 * u;
     return r * 128 + (((2 * rc) ^ (gr | (u & 6))) << 2);
   };
 
@@ -329,7 +411,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
     const uint16_t* Ao = ws + md.ws_a;
 #pragma unroll 8
     for (int u = 0; u < 32; ++u) {
-      const int r = (lane >> 4) + 4 * u;
+      const int r = (elane >> 4) + 4 * u;
       u32x4_t v = *reinterpret_cast<const u32x4_t*>(Ao + static_cast<int64_t>(i0w + r) * ldc +
                                                     j0w + 8 * rc);
       if (u & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
@@ -346,7 +428,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
   for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint16_t* Sjq = S + frow * 128 + ((((bj * 8 + 2 * q) ^ gacc) & 31) << 2);
+      uint16_t* Sjq = S + efrow * 128 + ((((bj * 8 + 2 * q) ^ gacc) & 31) << 2);
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         u32x2_t* slotp = reinterpret_cast<u32x2_t*>(Sjq + bi * 32 * 128);
@@ -362,7 +444,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
         }
         if (diag) {
           // a on the diagonal of B
-          const int il = bi * 32 + frow, jl = bj * 32 + 8 * q + 4 * hl;
+          const int il = bi * 32 + efrow, jl = bj * 32 + 8 * q + 4 * hl;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (i0w + il == j0w + jl + e) v[e] += g.a;
@@ -375,7 +457,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
   // row stores: 16 bytes per lane, 4 rows of 256 bytes per instruction
 #pragma unroll 8
   for (int u = 0; u < 32; ++u) {
-    const int r = (lane >> 4) + 4 * u;
+    const int r = (elane >> 4) + 4 * u;
     u32x4_t v = *reinterpret_cast<const u32x4_t*>(S + row_slot16(u));
     if (u & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
     *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(i0w + r) * ldc + j0w + 8 * rc) = v;
@@ -385,7 +467,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
     // C^T[j][i..i+7] = C[i..i+7][j] via two transpose reads per lane:
     // group G = lane/16 covers columns jb + 16*(G&1) + (lane%16) and rows
     // ib + 8*(G>>1) .. +7 of the staged tile.
-    const int s = lane & 15, G = lane >> 4;
+    const int s = elane & 15, G = elane >> 4;
 #pragma unroll 4
     for (int u = 0; u < 32; ++u) {
       const int jb = (u & 3) * 32, ib = (u >> 2) * 16;
@@ -406,16 +488,26 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const Item it, uint16
 // multiple of 8, so the 32 workgroups of an XCD still work on one group of
 // neighbouring tiles at a time; a tile's epilogue stores drain while the
 // next tile's first operand stages load.
+//
+// The tile list, the matrix table and the inverse norms come in as
+// __restrict__ parameters: they are read-only for the whole launch, so
+// their uniform loads become scalar loads, which do not wait for the
+// previous tile's stores (vector loads would: vmcnt counts loads and
+// stores together).
 template <int PHASE>
-__global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g) {
+__global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g, const Item* __restrict__ items,
+                                                    const MatDev* __restrict__ mats,
+                                                    const float* __restrict__ invs) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * 2 * BT * BK];  // 128 KiB
   bool busy = false;
   for (int idx = blockIdx.x; idx < g.n_items; idx += gridDim.x) {
-    const Item it = g.items[idx];
+    const Item it = items[idx];
     if (it.mat < 0) continue;  // padding of the XCD-grouped order
+    const MatDev md = mats[it.mat];
+    const float inv = g.first ? invs[md.widx] : 1.0f;
     if (busy) __syncthreads();  // the previous tile's epilogue is done with LDS
     busy = true;
-    ns_tile<PHASE>(g, it, smem);
+    ns_tile<PHASE>(g, md, it.rc >> 16, it.rc & 0xffff, inv, smem);
   }
 }
 
@@ -527,9 +619,12 @@ hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
   const dim3 block(256);
   if (ns_dtype == 1) {
     const dim3 grid(n_items < n_cu ? n_items : n_cu);
-    if (phase == 1) hipLaunchKernelGGL(k_ns_bf16<1>, grid, block, 0, s, args);
-    else if (phase == 2) hipLaunchKernelGGL(k_ns_bf16<2>, grid, block, 0, s, args);
-    else hipLaunchKernelGGL(k_ns_bf16<3>, grid, block, 0, s, args);
+    if (phase == 1)
+      hipLaunchKernelGGL(k_ns_bf16<1>, grid, block, 0, s, args, args.items, args.mats, args.inv);
+    else if (phase == 2)
+      hipLaunchKernelGGL(k_ns_bf16<2>, grid, block, 0, s, args, args.items, args.mats, args.inv);
+    else
+      hipLaunchKernelGGL(k_ns_bf16<3>, grid, block, 0, s, args, args.items, args.mats, args.inv);
   } else {
     const dim3 grid(n_items);
     if (phase == 1) hipLaunchKernelGGL(k_ns_f32<1>, grid, block, 0, s, args);
