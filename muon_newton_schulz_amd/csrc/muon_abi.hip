@@ -3,7 +3,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -357,6 +356,17 @@ muon::GemmArgs gemm_args(const muon_plan_t* p, const Wave& w, void* ws, const mu
   g.a = hp->ns_a;
   g.b = hp->ns_b;
   g.c = hp->ns_c;
+  // The bf16 engine's form of B = a I + b A + c A^2 (A = X X^T): with
+  // c == 0 phase 1 writes B = b A + a I directly (phase 2 is skipped);
+  // otherwise phase 1 writes A and phase 2 adds b A + a I to c A A.  (A
+  // shifted Gram matrix sqrt(c) A + beta I, whose square plus a multiple
+  // of I is B, would spare phase 2 its read of A, but its diagonal is
+  // dominated by beta and bf16 rounding then erases the Gram diagonal.)
+  const bool direct = hp->ns_c == 0.0f;
+  g.e1_scale = direct ? hp->ns_b : 1.0f;
+  g.e1_diag = direct ? hp->ns_a : 0.0f;
+  g.e2_scale = hp->ns_c;
+  g.e2_diag = hp->ns_a;
   g.first = iter == 0;
   g.x_cur = iter & 1;
   return g;

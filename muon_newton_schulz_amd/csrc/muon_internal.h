@@ -43,6 +43,10 @@ struct GemmArgs {
   void* ws;           // workspace base (NS element type)
   const float* inv;   // wave-local 1/(||U||_F + eps)
   float a, b, c;
+  // bf16 engine epilogue constants (host-computed from a, b, c):
+  //   phase 1 writes e1_scale * s2 * X X^T + e1_diag * I
+  //   phase 2 writes e2_scale * A A + b * A + e2_diag * I
+  float e1_scale, e1_diag, e2_scale, e2_diag;
   int32_t first;      // first NS iteration: fold the normalisation in
   int32_t x_cur;      // X buffer read by phases 1 and 3 (phase 3 writes 1 - x_cur)
   int32_t n_items;    // tile-list length (the persistent grid walks it)

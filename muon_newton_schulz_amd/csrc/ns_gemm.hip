@@ -52,7 +52,6 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_t;
-typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
 
 constexpr int BT = kTileBf16;  // 256
@@ -77,17 +76,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t)p));
 }
 
+// LDS fragment reads are issued as inline asm: the compiler's wait-count
+// pass would otherwise make every LDS read wait for all LDS DMA (and, for
+// the transpose read, all global stores) in flight, which drains the
+// pipelines.  Their completion is awaited explicitly (wait_frags,
+// wait_lds16) before use.  OFF is the instruction's immediate byte offset.
 // Transpose read: within each group of 16 lanes, lane l receives element
 // (l % 4) of the 8-byte blocks addressed by lanes 4q + l/4, q = 0..3.
-__device__ __forceinline__ s16x4_t ld_tr(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)p);
-}
-
-// Main-loop fragment reads are issued as inline asm: the compiler's
-// wait-count pass would otherwise make every LDS read wait for all LDS DMA
-// in flight (vmcnt(0)), which drains the load pipeline.  Their completion
-// is awaited explicitly with wait_frags before use.  OFF is the
-// instruction's immediate byte offset.
 template <int OFF>
 __device__ __forceinline__ s16x4_t ld_tr_async(uint32_t addr) {
   s16x4_t r;
@@ -153,6 +148,16 @@ __device__ __forceinline__ void wait_frags_tr(s16x4_t* t, bf16x8_t* p) {
                : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]),
                  "+v"(t[6]), "+v"(t[7]), "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3])
                : "n"(N)
+               : "memory");
+}
+
+// All LDS reads done, tied to the 16 results (epilogue transpose reads).
+__device__ __forceinline__ void wait_lds16(s16x4_t* t) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]),
+                 "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]),
+                 "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               :
                : "memory");
 }
 
@@ -338,8 +343,12 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
       if constexpr (m < NR) issue_read(F[1], sb, Int<1>{}, Int<m>{});
       __builtin_amdgcn_sched_barrier(0);
     });
-    wait_stage_landed(kt + 1, min(kt + NSLOT - 2, nk - 1));
-    pipe_barrier();
+    if constexpr (NEXT) {
+      // (the last stage has no next stage to wait for, and no slot is
+      // refilled after it)
+      wait_stage_landed(kt + 1, min(kt + NSLOT - 2, nk - 1));
+      pipe_barrier();
+    }
     settle(F[1]);
     __builtin_amdgcn_sched_barrier(0);
     const int rslot = (kt + NSLOT - 1) % NSLOT;
@@ -361,6 +370,20 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   int kt = 0;
   for (; kt + NSLOT - 1 < nk; ++kt) stage(kt, T_{}, T_{});
   for (; kt + 1 < nk; ++kt) stage(kt, F_{}, T_{});
+  // Phase 2's epilogue adds b*A: this wave's 128x128 sub-tile of A is
+  // loaded into registers while the last stage computes (16-byte row
+  // loads: row lane/16 + 4u, 16-byte chunk lane%16).
+  const int i0w = ti * BT + wi * 128, j0w = tj * BT + wj * 128;
+  constexpr bool aterm = PHASE == 2;
+  u32x4_t apre[32];
+  if constexpr (aterm) {
+    const int pl = opaque_lane(lane);
+    const uint16_t* Ao =
+        ws + md.ws_a + static_cast<int64_t>(i0w + (pl >> 4)) * md.m_pad + j0w + 8 * (pl & 15);
+#pragma unroll
+    for (int u = 0; u < 32; ++u)
+      apre[u] = *reinterpret_cast<const u32x4_t*>(Ao + static_cast<int64_t>(4 * u) * md.m_pad);
+  }
   stage(kt, F_{}, F_{});
   __syncthreads();
 
@@ -375,7 +398,6 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // (and spill).
   const int elane = opaque_lane(lane);
   uint16_t* S = smem + wave * (128 * 128);
-  const int i0w = ti * BT + wi * 128, j0w = tj * BT + wj * 128;
   uint16_t* C;
   int ldc;
   bool mirror;
@@ -406,24 +428,25 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     return r * 128 + (((2 * rc) ^ (gr | (u & 6))) << 2);
   };
 
-  if (PHASE == 2) {
-    // b*A term: stage this wave's A sub-tile in LDS (16-byte row loads)
-    const uint16_t* Ao = ws + md.ws_a;
-#pragma unroll 8
+  if constexpr (aterm) {
+    // b*A term: the prefetched A sub-tile into the staging layout
+#pragma unroll
     for (int u = 0; u < 32; ++u) {
-      const int r = (elane >> 4) + 4 * u;
-      u32x4_t v = *reinterpret_cast<const u32x4_t*>(Ao + static_cast<int64_t>(i0w + r) * ldc +
-                                                    j0w + 8 * rc);
+      u32x4_t v = apre[u];
       if (u & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
       *reinterpret_cast<u32x4_t*>(S + row_slot16(u)) = v;
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // values -> LDS staging (8-byte slots)
   const float s2 = inv * inv;
-  const bool diag = ti == tj && PHASE != 3 && (PHASE == 2 || g.c == 0.0f);
-  const float sc = PHASE == 1 ? (g.c != 0.0f ? 1.0f : g.b) * s2 : PHASE == 2 ? g.c : inv;
+  const float sc = PHASE == 1 ? g.e1_scale * s2 : PHASE == 2 ? g.e2_scale : inv;
+  // diagonal term: only a wave sub-tile on the diagonal (ti == tj,
+  // wi == wj) has one, in its blocks bi == bj, where element (il, jl + e)
+  // is diagonal iff frow == 8q + 4*hl + e
+  const float dval =
+      (PHASE != 3 && ti == tj && wi == wj) ? (PHASE == 1 ? g.e1_diag : g.e2_diag) : 0.0f;
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
@@ -435,19 +458,16 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
         f32x4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = sc * acc[bj][bi][4 * q + e];
-        if (PHASE == 2) {
+        if constexpr (aterm) {
           const u32x2_t a0 = *slotp;
           v[0] += g.b * lo_bf(a0[0]);
           v[1] += g.b * hi_bf(a0[0]);
           v[2] += g.b * lo_bf(a0[1]);
           v[3] += g.b * hi_bf(a0[1]);
         }
-        if (diag) {
-          // a on the diagonal of B
-          const int il = bi * 32 + efrow, jl = bj * 32 + 8 * q + 4 * hl;
+        if (PHASE != 3 && bi == bj) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (i0w + il == j0w + jl + e) v[e] += g.a;
+          for (int e = 0; e < 4; ++e) v[e] += efrow == 8 * q + 4 * hl + e ? dval : 0.0f;
         }
         *slotp = u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])};
       }
@@ -466,19 +486,31 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   if (mirror) {
     // C^T[j][i..i+7] = C[i..i+7][j] via two transpose reads per lane:
     // group G = lane/16 covers columns jb + 16*(G&1) + (lane%16) and rows
-    // ib + 8*(G>>1) .. +7 of the staged tile.
+    // ib + 8*(G>>1) .. +7 of the staged tile.  Eight rows of output per
+    // batch: 16 reads in flight, one wait, 8 stores.
     const int s = elane & 15, G = elane >> 4;
-#pragma unroll 4
-    for (int u = 0; u < 32; ++u) {
-      const int jb = (u & 3) * 32, ib = (u >> 2) * 16;
-      const int ir = ib + 8 * (G >> 1) + (s >> 2);
-      const int jc = jb + 16 * (G & 1) + 4 * (s & 3);
-      const s16x4_t lo = ld_tr(S + stg(ir, jc));
-      const s16x4_t hi = ld_tr(S + stg(ir + 4, jc));
-      const int jo = jb + 16 * (G & 1) + s;
-      const int io = ib + 8 * (G >> 1);
-      *reinterpret_cast<s16x8_t*>(C + static_cast<int64_t>(j0w + jo) * ldc + i0w + io) =
-          __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    const uint32_t sbase = lds_addr(S);
+    for (int u0 = 0; u0 < 32; u0 += 8) {
+      s16x4_t tr[16];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int u = u0 + v;
+        const int jb = (u & 3) * 32, ib = (u >> 2) * 16;
+        const int ir = ib + 8 * (G >> 1) + (s >> 2);
+        const int jc = jb + 16 * (G & 1) + 4 * (s & 3);
+        tr[2 * v] = ld_tr_async<0>(sbase + 2 * stg(ir, jc));
+        tr[2 * v + 1] = ld_tr_async<0>(sbase + 2 * stg(ir + 4, jc));
+      }
+      wait_lds16(tr);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int u = u0 + v;
+        const int jb = (u & 3) * 32, ib = (u >> 2) * 16;
+        const int jo = jb + 16 * (G & 1) + s;
+        const int io = ib + 8 * (G >> 1);
+        *reinterpret_cast<s16x8_t*>(C + static_cast<int64_t>(j0w + jo) * ldc + i0w + io) =
+            __builtin_shufflevector(tr[2 * v], tr[2 * v + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     }
   }
 }
