@@ -46,6 +46,22 @@ def measured_traffic(workload):
     return data["fetch_bytes_per_launch"] + data["write_bytes_per_launch"]
 
 
+def mfma_ceiling():
+    """Sustained bf16 MFMA rate of this GPU (muon_newton_schulz_amd/mfma_ceiling:
+    back-to-back MFMAs from registers on every SIMD, no memory traffic), or
+    None if the program is missing or fails.  Run as a child process after
+    the timed region."""
+    import subprocess
+    exe = os.path.join(ROOT, "muon_newton_schulz_amd", "mfma_ceiling")
+    if not os.path.exists(exe):
+        return None
+    try:
+        res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        return json.loads(res.stdout.strip().splitlines()[-1]) if res.returncode == 0 else None
+    except (OSError, ValueError, IndexError, subprocess.TimeoutExpired):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +237,8 @@ def main():
     copy_gbps = 5 * 2 * (1 << 30) / (a.elapsed_time(b_) * 1e-3) / 1e9
     del src, dst
 
+    ceiling = mfma_ceiling()
+
     # ---- algorithmic work
     shapes = wl.shapes
     mm = [(min(r, c), max(r, c)) for r, c in shapes]
@@ -275,6 +293,10 @@ def main():
                             "by a plain-copy calibration)",
             "flops_per_launch": f3,
             "avg_launch_ms": k["ns3"][0],
+            # the same GPU's sustained MFMA-only rate (clock under its own
+            # power management), measured after the timed region
+            "sustained_mfma_ceiling": ceiling,
+            "frac_of_sustained_ceiling": (f3_tflops / ceiling["tflops"]) if ceiling else None,
         },
         "breakdown_ms_per_step": {
             "momentum+norm": k["momentum"][0] * k["momentum"][1],

@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmuon.so")
 SOURCES = ["muon_abi.hip", "elementwise.hip", "ns_gemm.hip"]
+# stand-alone measurement program: the GPU's sustained bf16 MFMA rate
+CEILING = os.path.join(PKG, "mfma_ceiling")
+CEILING_SRC = "mfma_ceiling.hip"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -32,10 +35,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = True) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+def _hipcc(cmd, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [*cmd, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,7 +47,14 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    _hipcc([HIPCC, *FLAGS, *srcs], LIB, verbose)
+    exe_flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    _hipcc([HIPCC, *exe_flags, os.path.join(CSRC, CEILING_SRC)], CEILING, verbose)
     return LIB
 
 
