@@ -171,6 +171,8 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     d.trans = d.rows > d.cols ? 1 : 0;
     d.m_pad = static_cast<int32_t>(round_up(std::min(d.rows, d.cols), T));
     d.n_pad = static_cast<int32_t>(round_up(std::max(d.rows, d.cols), T));
+    d.m_k = static_cast<int32_t>(round_up(std::min(d.rows, d.cols), muon::kNsKStep));
+    d.n_k = static_cast<int32_t>(round_up(std::max(d.rows, d.cols), muon::kNsKStep));
     const double m = std::min(d.rows, d.cols), n = std::max(d.rows, d.cols);
     p.flops_per_iter += m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n;
   }

@@ -11,6 +11,7 @@ constexpr int kEwTile = 64;
 // GEMM tile edges: bf16 MFMA engine and fp32 engine.
 constexpr int kTileBf16 = 256;
 constexpr int kTileFp32 = 64;
+constexpr int kNsKStep = 32;  // bf16 engine: K per pipeline stage
 
 // One matrix of a plan, as the device sees it.  "Oriented" dims put the
 // short side first (m = min(rows, cols), n = max(rows, cols)); tall
@@ -21,6 +22,8 @@ struct MatDev {
   int64_t off;      // element offset in the flat params/grads/momentum
   int32_t rows, cols;
   int32_t m_pad, n_pad;  // oriented, padded to the GEMM tile
+  int32_t m_k, n_k;      // m, n rounded up to the bf16 engine's K step: the
+                         // contraction extents (the padding beyond is zero)
   int32_t trans;         // 1 if rows > cols
   int32_t widx;          // index of the matrix within its wave
   int32_t k1_begin;      // first elementwise tile of this matrix (wave-local)

@@ -55,7 +55,7 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
 
 constexpr int BT = kTileBf16;  // 256
-constexpr int BK = 32;           // K per pipeline stage
+constexpr int BK = kNsKStep;     // K per pipeline stage (32)
 constexpr int NSLOT = 4;         // LDS ring slots (stages in flight: NSLOT - 1)
 constexpr int DMA_PER_STAGE = 8;  // DMA instructions per wave per stage
 
@@ -192,16 +192,21 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // operands
   const uint16_t *P, *Q;
   int ldp, ldq, K;
+  // K runs over the true extent rounded to the K step only: the rest of
+  // the padded operands is zero
   if (PHASE == 1) {
-    ldp = ldq = K = md.n_pad;
+    ldp = ldq = md.n_pad;
+    K = md.n_k;
     P = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(ti) * BT * ldp;
     Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * BT * ldq;
   } else if (PHASE == 2) {
-    ldp = ldq = K = md.m_pad;
+    ldp = ldq = md.m_pad;
+    K = md.m_k;
     P = ws + md.ws_a + static_cast<int64_t>(ti) * BT * ldp;
     Q = ws + md.ws_a + static_cast<int64_t>(tj) * BT * ldq;
   } else {
-    ldp = K = md.m_pad;
+    ldp = md.m_pad;
+    K = md.m_k;
     ldq = md.n_pad;
     P = ws + md.ws_b + static_cast<int64_t>(ti) * BT * ldp;
     Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * BT;  // column block of [k][j]
