@@ -197,14 +197,17 @@ def update_scale(rows: int, cols: int, mode: int, rms_target: float) -> float:
 
 
 def muon_matrix_math(W: np.ndarray, G: np.ndarray, M: np.ndarray,
-                     hp: MuonHP) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                     hp: MuonHP, grad_scale: float = 1.0
+                     ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Muon step for one matrix, in fp64, no storage rounding.
 
     Returns (W_new, M_new, O) where O is the orthogonalised update.
     The order (momentum, normalise, NS, apply) is reading R3 / R7.
+    ``grad_scale`` multiplies the gradient first (the clip factor of a
+    clipped step, oracle/guard_oracle.py reading G2).
     """
     W = np.asarray(W, dtype=np.float64)
-    G = np.asarray(G, dtype=np.float64)
+    G = grad_scale * np.asarray(G, dtype=np.float64)
     M = np.asarray(M, dtype=np.float64)
     rows, cols = W.shape
     M_new = ema_momentum(M, G, hp.momentum)
@@ -218,7 +221,8 @@ def muon_matrix_math(W: np.ndarray, G: np.ndarray, M: np.ndarray,
 
 def muon_step_flat(params: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
                    mats: Sequence[Tuple[int, int, int]], hp: MuonHP,
-                   param_dtype: str, only: Sequence[int] | None = None
+                   param_dtype: str, only: Sequence[int] | None = None,
+                   grad_scale: float = 1.0
                    ) -> Tuple[np.ndarray, np.ndarray, Dict[int, np.ndarray]]:
     """Muon step over a flat concatenated buffer ([K2] 2.2: all parameters
     flattened and concatenated; each matrix addressed by its element offset).
@@ -226,6 +230,7 @@ def muon_step_flat(params: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
     ``mats`` holds (offset, rows, cols) per matrix, row-major.  Elements not
     covered by a matrix are left untouched.  ``only`` restricts the work to
     the listed matrix indices (sampled parity at large sizes).
+    ``grad_scale`` multiplies every gradient (a clipped step).
     Returns (params_new, momentum_new, {index: O}) with params rounded to
     ``param_dtype`` and momentum to fp32, once, at the end of the step.
     """
@@ -239,7 +244,7 @@ def muon_step_flat(params: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
         sl = slice(off, off + r * c)
         W_new, M_new, O = muon_matrix_math(p[sl].reshape(r, c),
                                            g[sl].reshape(r, c),
-                                           mom[sl].reshape(r, c), hp)
+                                           mom[sl].reshape(r, c), hp, grad_scale)
         p[sl] = round_to(W_new, param_dtype).reshape(-1)
         mom[sl] = fp32_round(M_new).reshape(-1)
         outs[i] = O
@@ -263,17 +268,19 @@ def ns_flops(rows: int, cols: int, steps: int, c: float) -> float:
 
 
 def adamw_math(theta: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray,
-               hp: AdamWHP, t: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+               hp: AdamWHP, t: int, grad_scale: float = 1.0
+               ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """One AdamW step in fp64, as printed (reading R8).  t >= 1.
 
     m <- b1 m + (1-b1) g ; v <- b2 v + (1-b2) g^2
     m_hat = m/(1-b1^t) ; v_hat = v/(1-b2^t)
     theta <- theta - lr*m_hat/(sqrt(v_hat)+eps) - lr*wd*theta_old
+    ``grad_scale`` multiplies g first (a clipped step).
     """
     if t < 1:
         raise ValueError("AdamW step count starts at 1")
     theta = np.asarray(theta, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
+    g = grad_scale * np.asarray(g, dtype=np.float64)
     m_new = hp.beta1 * np.asarray(m, dtype=np.float64) + (1.0 - hp.beta1) * g
     v_new = hp.beta2 * np.asarray(v, dtype=np.float64) + (1.0 - hp.beta2) * g * g
     m_hat = m_new / (1.0 - hp.beta1 ** t)
@@ -285,7 +292,7 @@ def adamw_math(theta: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray,
 
 def adamw_step_stored(param: np.ndarray, master: np.ndarray | None,
                       g: np.ndarray, m: np.ndarray, v: np.ndarray,
-                      hp: AdamWHP, t: int, param_dtype: str
+                      hp: AdamWHP, t: int, param_dtype: str, grad_scale: float = 1.0
                       ) -> Tuple[np.ndarray, np.ndarray | None, np.ndarray, np.ndarray]:
     """AdamW step with storage rounding ([OPT] 3.3, reading R9).
 
@@ -295,7 +302,7 @@ def adamw_step_stored(param: np.ndarray, master: np.ndarray | None,
     Returns (param_new, master_new or None, m_new, v_new).
     """
     theta = master if master is not None else param
-    th, m_new, v_new = adamw_math(theta, g, m, v, hp, t)
+    th, m_new, v_new = adamw_math(theta, g, m, v, hp, t, grad_scale)
     th32 = fp32_round(th)
     if master is not None:
         return round_to(th32, param_dtype), th32, fp32_round(m_new), fp32_round(v_new)
