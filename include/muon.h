@@ -14,6 +14,10 @@
  *         norm is bounded by the Frobenius norm.
  *   [EP]  aihot.vn news item on MoonEP, "memory contract": expert weights
  *         live in one contiguous [E, H, H'] tensor addressed by row offset.
+ *   [OPT] 5.4 (optimizer numerical faults under mixed precision): keep
+ *         gradient clipping (clip_grad_norm) as a safety net, guard the
+ *         step against Inf/NaN by skipping it, and watch statistics of the
+ *         optimizer state (mean and variance of m, collapse of v).
  *
  * Conventions for every call:
  *   - Returns MUON_OK (0) or a negative MUON_ERR_* code; nothing throws.
@@ -26,7 +30,8 @@
  *     synchronises.  A kernel fault surfaces at the caller's next
  *     synchronisation of that stream.
  *   - Buffers passed to one call must not alias each other.
- *   - Non-finite inputs propagate into the outputs; there is no guard.
+ *   - Non-finite inputs propagate into the outputs unless the step is
+ *     guarded through a clip state (grad_norm_clip below).
  */
 #ifndef MUON_H_
 #define MUON_H_
@@ -74,6 +79,21 @@ typedef struct {
  *   scale_mode       : s = rms_target*sqrt(max(r,c)) (0, [K2] 3.1),
  *                      sqrt(max(1, r/c)) (1, [K2] 3.2), 1 (2)
  */
+/* Result of grad_norm_clip, resident in device memory ([OPT] 5.4):
+ *   norm  : global L2 norm of all the gradients given (fp64 sum of squares)
+ *   scale : min(1, max_norm / (norm + eps)), the factor every gradient is
+ *           multiplied by before the step; 1 when clipping is off
+ *   skip  : 1 when the norm is not finite (a NaN or Inf gradient): a step
+ *           given this state changes no parameter and no state buffer
+ * The steps read it on the device, so clipping and the guard need no host
+ * synchronisation. */
+typedef struct {
+  float norm;
+  float scale;
+  int32_t skip;
+  int32_t reserved;
+} muon_clip_state_t;
+
 typedef struct {
   float lr;
   float weight_decay;
@@ -86,6 +106,10 @@ typedef struct {
   float eps;
   int32_t scale_mode;
   float rms_target;
+  /* nullable device pointer: gradient scale and step guard from
+   * grad_norm_clip; read by muon_step, muon_stage_momentum (scale, skip)
+   * and muon_stage_apply (skip) */
+  const muon_clip_state_t* clip;
 } muon_hparams_t;
 
 /* Hyperparameters of one AdamW step ([OPT] 2.3, 3.1). */
@@ -95,6 +119,8 @@ typedef struct {
   float beta2;
   float eps;
   float weight_decay;
+  /* nullable device pointer: gradient scale and step guard (see above) */
+  const muon_clip_state_t* clip;
 } adamw_hparams_t;
 
 /* Opaque plan: matrix descriptors validated, orientation (tall matrices
@@ -144,6 +170,8 @@ int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info);
  *   out_update : nullable flat fp32; receives O (the orthogonalised update
  *                before scaling) at each matrix's elements
  * Elements of the flat buffers not covered by a matrix are never touched.
+ * With hp->clip set, every gradient is multiplied by clip->scale, and if
+ * clip->skip is set params, momentum and out_update are left unchanged.
  * Concurrent steps on one workspace race; use one workspace per stream. */
 int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* momentum,
               void* workspace, size_t workspace_bytes, const muon_hparams_t* hp,
@@ -185,10 +213,60 @@ int muon_stage_export_norms(const muon_plan_t* plan, int32_t wave, const void* w
  * master null: params must be fp32 and is theta itself.
  * grads: grad_dtype.  exp_avg, exp_avg_sq: fp32, updated in place.
  * step: 1-based t; the bias corrections are formed in fp64 on the host.
+ * With hp->clip set, g is multiplied by clip->scale, and if clip->skip is
+ * set nothing is written (the caller keeps t for the next step).
  * No alignment is required beyond the element size. */
 int adamw_step(void* params, int32_t param_dtype, float* master, const void* grads,
                int32_t grad_dtype, float* exp_avg, float* exp_avg_sq, int64_t n,
                const adamw_hparams_t* hp, int64_t step, hipStream_t stream);
+
+/* ---- gradient clipping, step guard, state statistics ([OPT] 5.4) ------ */
+
+/* One device buffer of gradients for the global norm: n elements of dtype. */
+typedef struct {
+  const void* ptr;
+  int64_t n;
+  int32_t dtype;
+  int32_t reserved;
+} muon_grad_buffer_t;
+
+/* Device workspace grad_norm_clip needs for n_bufs buffers. */
+size_t grad_norm_clip_workspace_size(int32_t n_bufs);
+
+/* Global gradient-norm clipping and the non-finite guard ([OPT] 5.4):
+ * norm = sqrt(sum over every element of every buffer of g^2), accumulated
+ * in fp64 in a fixed order (bitwise reproducible); scale = min(1,
+ * max_norm / (norm + eps)), or 1 if max_norm <= 0; skip = norm not finite.
+ * Writes *out (device memory).  Pass `out` as the `clip` field of the
+ * Muon and AdamW hyperparameters of the same step.  bufs is a host array;
+ * buffers with n == 0 may have a null ptr.  workspace: device memory of at
+ * least grad_norm_clip_workspace_size(n_bufs) bytes, 8-byte aligned. */
+int grad_norm_clip(const muon_grad_buffer_t* bufs, int32_t n_bufs, float max_norm, float eps,
+                   void* workspace, size_t workspace_bytes, muon_clip_state_t* out,
+                   hipStream_t stream);
+
+/* Statistics of one fp32 optimizer-state buffer ([OPT] 5.4, the state
+ * monitoring of the closing notes), over its finite elements: count, mean,
+ * population variance, min, max, max |x|; plus the number of NaN and +-Inf
+ * elements.  All six values are 0 over no finite element.  fp64
+ * accumulation in a fixed order (bitwise reproducible). */
+typedef struct {
+  double mean;
+  double var;
+  double min;
+  double max;
+  double absmax;
+  int64_t count;
+  int64_t nonfinite;
+} muon_state_stats_t;
+
+/* Device workspace state_stats needs. */
+size_t state_stats_workspace_size(void);
+
+/* Writes *out (device memory).  x: n fp32 elements.  workspace: at least
+ * state_stats_workspace_size() bytes, 8-byte aligned. */
+int state_stats(const float* x, int64_t n, void* workspace, size_t workspace_bytes,
+                muon_state_stats_t* out, hipStream_t stream);
 
 const char* muon_status_string(int32_t status);
 const char* muon_last_error(void);

@@ -33,7 +33,8 @@ EXPORTED = [
     "muon_workspace_size", "muon_plan_create", "muon_plan_destroy", "muon_plan_get_info",
     "muon_step", "muon_stage_momentum", "muon_stage_ns_phase", "muon_stage_apply",
     "muon_stage_export_x", "muon_stage_export_norms", "adamw_step", "muon_status_string",
-    "muon_last_error",
+    "muon_last_error", "grad_norm_clip_workspace_size", "grad_norm_clip",
+    "state_stats_workspace_size", "state_stats",
 ]
 
 
@@ -52,12 +53,32 @@ class MuonHParamsC(ctypes.Structure):
                 ("momentum", ctypes.c_float), ("nesterov", ctypes.c_int32),
                 ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
                 ("ns_steps", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("scale_mode", ctypes.c_int32), ("rms_target", ctypes.c_float)]
+                ("scale_mode", ctypes.c_int32), ("rms_target", ctypes.c_float),
+                ("clip", ctypes.c_void_p)]
 
 
 class AdamWHParamsC(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
-                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("clip", ctypes.c_void_p)]
+
+
+class MuonClipState(ctypes.Structure):
+    """Host view of muon_clip_state_t (the device copy lives in a 16-byte tensor)."""
+    _fields_ = [("norm", ctypes.c_float), ("scale", ctypes.c_float), ("skip", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class MuonGradBuffer(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("n", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class MuonStateStats(ctypes.Structure):
+    """Host view of muon_state_stats_t."""
+    _fields_ = [("mean", ctypes.c_double), ("var", ctypes.c_double), ("min", ctypes.c_double),
+                ("max", ctypes.c_double), ("absmax", ctypes.c_double),
+                ("count", ctypes.c_int64), ("nonfinite", ctypes.c_int64)]
 
 
 class MuonPlanInfo(ctypes.Structure):
@@ -96,12 +117,20 @@ def lib() -> ctypes.CDLL:
     L.muon_stage_export_x.argtypes = [P, I32, P, SZ, I32, P, P]
     L.muon_stage_export_norms.argtypes = [P, I32, P, SZ, P, P]
     L.adamw_step.argtypes = [P, I32, P, P, I32, P, P, I64, ctypes.POINTER(AdamWHParamsC), I64, P]
+    L.grad_norm_clip_workspace_size.argtypes = [I32]
+    L.grad_norm_clip_workspace_size.restype = SZ
+    L.grad_norm_clip.argtypes = [ctypes.POINTER(MuonGradBuffer), I32, ctypes.c_float,
+                                 ctypes.c_float, P, SZ, P, P]
+    L.state_stats_workspace_size.argtypes = []
+    L.state_stats_workspace_size.restype = SZ
+    L.state_stats.argtypes = [P, I64, P, SZ, P, P]
     L.muon_status_string.argtypes = [I32]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_last_error.argtypes = []
     L.muon_last_error.restype = ctypes.c_char_p
     for name in EXPORTED:
-        if name not in ("muon_plan_destroy", "muon_status_string", "muon_last_error"):
+        if name not in ("muon_plan_destroy", "muon_status_string", "muon_last_error",
+                        "grad_norm_clip_workspace_size", "state_stats_workspace_size"):
             getattr(L, name).restype = ctypes.c_int
     _lib_handle = L
     return L
@@ -154,20 +183,28 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def _hp(hp) -> MuonHParamsC:
+def _hp(hp, clip=None) -> MuonHParamsC:
     if isinstance(hp, MuonHParamsC):
-        return hp
-    return MuonHParamsC(float(hp.lr), float(hp.weight_decay), float(hp.momentum),
-                        int(bool(hp.nesterov)), float(hp.ns_a), float(hp.ns_b),
-                        float(hp.ns_c), int(hp.ns_steps), float(hp.eps), int(hp.scale_mode),
-                        float(hp.rms_target))
+        h = MuonHParamsC.from_buffer_copy(hp)
+    else:
+        h = MuonHParamsC(float(hp.lr), float(hp.weight_decay), float(hp.momentum),
+                         int(bool(hp.nesterov)), float(hp.ns_a), float(hp.ns_b),
+                         float(hp.ns_c), int(hp.ns_steps), float(hp.eps), int(hp.scale_mode),
+                         float(hp.rms_target))
+    if clip is not None:
+        h.clip = _ptr(clip)
+    return h
 
 
-def _ahp(hp) -> AdamWHParamsC:
+def _ahp(hp, clip=None) -> AdamWHParamsC:
     if isinstance(hp, AdamWHParamsC):
-        return hp
-    return AdamWHParamsC(float(hp.lr), float(hp.beta1), float(hp.beta2), float(hp.eps),
-                         float(hp.weight_decay))
+        h = AdamWHParamsC.from_buffer_copy(hp)
+    else:
+        h = AdamWHParamsC(float(hp.lr), float(hp.beta1), float(hp.beta2), float(hp.eps),
+                          float(hp.weight_decay))
+    if clip is not None:
+        h.clip = _ptr(clip)
+    return h
 
 
 # ---------------------------------------------------------------- plan
@@ -231,16 +268,17 @@ def muon_plan_get_info(plan: MuonPlan) -> MuonPlanInfo:
 
 
 def muon_step(plan: MuonPlan, params, grads, momentum, workspace, hp, out_update=None,
-              stream=None) -> None:
-    h = _hp(hp)
+              stream=None, clip=None) -> None:
+    """clip: optional device clip state from grad_norm_clip (scale and guard)."""
+    h = _hp(hp, clip)
     _check(lib().muon_step(ctypes.c_void_p(plan.handle), _ptr(params), _ptr(grads),
                            _ptr(momentum), _ptr(workspace), workspace.numel(), ctypes.byref(h),
                            _ptr(out_update), _stream(stream)))
 
 
 def muon_stage_momentum(plan: MuonPlan, wave: int, grads, momentum, workspace, hp,
-                        stream=None) -> None:
-    h = _hp(hp)
+                        stream=None, clip=None) -> None:
+    h = _hp(hp, clip)
     _check(lib().muon_stage_momentum(ctypes.c_void_p(plan.handle), wave, _ptr(grads),
                                      _ptr(momentum), _ptr(workspace), workspace.numel(),
                                      ctypes.byref(h), _stream(stream)))
@@ -255,8 +293,8 @@ def muon_stage_ns_phase(plan: MuonPlan, wave: int, workspace, hp, iter: int, pha
 
 
 def muon_stage_apply(plan: MuonPlan, wave: int, params, workspace, hp, out_update=None,
-                     stream=None) -> None:
-    h = _hp(hp)
+                     stream=None, clip=None) -> None:
+    h = _hp(hp, clip)
     _check(lib().muon_stage_apply(ctypes.c_void_p(plan.handle), wave, _ptr(params),
                                   _ptr(workspace), workspace.numel(), ctypes.byref(h),
                                   _ptr(out_update), _stream(stream)))
@@ -273,14 +311,75 @@ def muon_stage_export_norms(plan: MuonPlan, wave: int, workspace, out, stream=No
                                          workspace.numel(), _ptr(out), _stream(stream)))
 
 
-def adamw_step(params, master, grads, exp_avg, exp_avg_sq, hp, step: int, stream=None) -> None:
-    """params/grads may be bf16 or fp32 tensors; master (fp32) may be None."""
+def adamw_step(params, master, grads, exp_avg, exp_avg_sq, hp, step: int, stream=None,
+               clip=None) -> None:
+    """params/grads may be bf16 or fp32 tensors; master (fp32) may be None;
+    clip: optional device clip state from grad_norm_clip."""
     n = params.numel()
     for name, t in (("grads", grads), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq),
                     ("master", master)):
         if t is not None and t.numel() != n:
             raise MuonError(MUON_ERR_INVALID_ARG, f"{name} has {t.numel()} elements, expected {n}")
-    h = _ahp(hp)
+    h = _ahp(hp, clip)
     _check(lib().adamw_step(_ptr(params), dtype_code(params.dtype), _ptr(master), _ptr(grads),
                             dtype_code(grads.dtype), _ptr(exp_avg), _ptr(exp_avg_sq), n,
                             ctypes.byref(h), int(step), _stream(stream)))
+
+
+# ------------------------------------------ clipping, step guard, statistics
+
+def grad_norm_clip_workspace_size(n_bufs: int) -> int:
+    return int(lib().grad_norm_clip_workspace_size(int(n_bufs)))
+
+
+def grad_norm_clip(grads: Sequence, max_norm: float, eps: float = 1e-6, out=None,
+                   workspace=None, stream=None):
+    """Global gradient norm over the given tensors, clip scale and skip flag,
+    written to ``out`` (a 16-byte device tensor, allocated if None) and
+    returned; pass it as ``clip=`` to the steps of the same iteration."""
+    import torch
+    bufs = (MuonGradBuffer * max(1, len(grads)))()
+    dev = None
+    for k, g in enumerate(grads):
+        bufs[k] = MuonGradBuffer(_ptr(g), int(g.numel()), dtype_code(g.dtype), 0)
+        dev = g.device
+    dev = dev if dev is not None else torch.device("cuda")
+    if out is None:
+        out = torch.zeros(16, dtype=torch.uint8, device=dev)
+    need = grad_norm_clip_workspace_size(len(grads))
+    if workspace is None:
+        workspace = torch.empty(max(8, need), dtype=torch.uint8, device=dev)
+    _check(lib().grad_norm_clip(bufs, len(grads), float(max_norm), float(eps), _ptr(workspace),
+                                workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def read_clip_state(out) -> dict:
+    """Copy a device clip state to the host (synchronises)."""
+    c = MuonClipState.from_buffer_copy(bytes(out.cpu().numpy().tobytes()))
+    return {"norm": c.norm, "scale": c.scale, "skip": bool(c.skip)}
+
+
+def state_stats_workspace_size() -> int:
+    return int(lib().state_stats_workspace_size())
+
+
+def state_stats(x, out=None, workspace=None, stream=None):
+    """Statistics of a fp32 state tensor into ``out`` (a 56-byte device
+    tensor, allocated if None), returned."""
+    import torch
+    if x.dtype != torch.float32:
+        raise MuonError(MUON_ERR_BAD_DTYPE, "state_stats takes fp32 buffers")
+    if out is None:
+        out = torch.zeros(ctypes.sizeof(MuonStateStats), dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(state_stats_workspace_size(), dtype=torch.uint8, device=x.device)
+    _check(lib().state_stats(_ptr(x), int(x.numel()), _ptr(workspace), workspace.numel(),
+                             _ptr(out), _stream(stream)))
+    return out
+
+
+def read_state_stats(out) -> dict:
+    """Copy device statistics to the host (synchronises)."""
+    s = MuonStateStats.from_buffer_copy(bytes(out.cpu().numpy().tobytes()))
+    return {k: getattr(s, k) for k, _ in MuonStateStats._fields_}

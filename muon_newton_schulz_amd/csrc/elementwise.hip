@@ -104,9 +104,16 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
                                                   const GT* __restrict__ grads,
                                                   float* __restrict__ mom, UT* __restrict__ ws,
                                                   float* __restrict__ partials, float mu,
-                                                  int nesterov, int bufs_aligned) {
+                                                  int nesterov, int bufs_aligned,
+                                                  const ClipState* __restrict__ clip) {
   __shared__ float tile[kEwTile][kEwTile + 1];
   __shared__ float wsum[4];
+  // guarded step: skip it whole, or scale the gradient (uniform branch)
+  float gscale = 1.0f;
+  if (clip != nullptr) {
+    if (clip->skip) return;
+    gscale = clip->scale;
+  }
   const Item it = items[blockIdx.x];
   const MatDev md = mats[it.mat];
   const int r0 = (it.rc >> 16) * kEwTile, c0 = (it.rc & 0xffff) * kEwTile;
@@ -123,7 +130,7 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
       f32x4v u = {0.f, 0.f, 0.f, 0.f};
       if (r < md.rows && c < md.cols) {
         const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
-        const f32x4v g = V4<GT>::ld(grads, e);
+        const f32x4v g = gscale * V4<GT>::ld(grads, e);
         f32x4v m = V4<float>::ld(mom, e);
         m = mu * m + omm * g;
         V4<float>::st(mom, e, m);
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
       float u = 0.0f;
       if (r < md.rows && c < md.cols) {
         const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
-        const float g = Elem<GT>::ld(grads, e);
+        const float g = gscale * Elem<GT>::ld(grads, e);
         const float m = mu * mom[e] + omm * g;
         mom[e] = m;
         u = nesterov ? mu * m + omm * g : m;
@@ -247,8 +254,10 @@ __global__ __launch_bounds__(256) void k_apply(const MatDev* __restrict__ mats,
                                                const float* __restrict__ inv, int use_inv,
                                                int x_final, float lr, float wd, int scale_mode,
                                                float rms_target, float* __restrict__ out_update,
-                                               int bufs_aligned) {
+                                               int bufs_aligned,
+                                               const ClipState* __restrict__ clip) {
   __shared__ float tile[kEwTile][kEwTile + 1];
+  if (clip != nullptr && clip->skip) return;  // guarded step: nothing changes
   const Item it = items[blockIdx.x];
   const MatDev md = mats[it.mat];
   const int r0 = (it.rc >> 16) * kEwTile, c0 = (it.rc & 0xffff) * kEwTile;
@@ -333,8 +342,9 @@ __global__ __launch_bounds__(256) void k_export(const MatDev* __restrict__ mats,
 template <typename PT, typename GT, bool MASTER>
 __device__ __forceinline__ void adamw_one(PT* params, float* master, const GT* grads, float* m,
                                           float* v, int64_t i, float b1, float b2, float eps,
-                                          float lr_bc1, float rsqrt_bc2, float decay) {
-  const float g = Elem<GT>::ld(grads, i);
+                                          float lr_bc1, float rsqrt_bc2, float decay,
+                                          float gscale) {
+  const float g = gscale * Elem<GT>::ld(grads, i);
   const float th = MASTER ? master[i] : Elem<PT>::ld(params, i);
   const float mm = b1 * m[i] + (1.0f - b1) * g;
   const float vv = b2 * v[i] + (1.0f - b2) * g * g;
@@ -354,12 +364,18 @@ __global__ __launch_bounds__(256) void k_adamw_scalar(PT* __restrict__ params,
                                                       float* __restrict__ m, float* __restrict__ v,
                                                       int64_t n, float b1, float b2, float eps,
                                                       float lr_bc1, float rsqrt_bc2,
-                                                      float decay) {
+                                                      float decay,
+                                                      const ClipState* __restrict__ clip) {
+  float gscale = 1.0f;
+  if (clip != nullptr) {
+    if (clip->skip) return;  // guarded step: nothing changes
+    gscale = clip->scale;
+  }
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += stride)
     adamw_one<PT, GT, MASTER>(params, master, grads, m, v, i, b1, b2, eps, lr_bc1, rsqrt_bc2,
-                              decay);
+                              decay, gscale);
 }
 
 // 8 consecutive elements per thread and iteration: bf16 vectors are 16
@@ -407,13 +423,21 @@ __global__ __launch_bounds__(256) void k_adamw_vec8(PT* __restrict__ params,
                                                     const GT* __restrict__ grads,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     int64_t n, float b1, float b2, float eps,
-                                                    float lr_bc1, float rsqrt_bc2, float decay) {
+                                                    float lr_bc1, float rsqrt_bc2, float decay,
+                                                    const ClipState* __restrict__ clip) {
+  float gscale = 1.0f;
+  if (clip != nullptr) {
+    if (clip->skip) return;  // guarded step: nothing changes
+    gscale = clip->scale;
+  }
   const int64_t n8 = n >> 3;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < n8;
        q += stride) {
     float g[8], th[8], mm[8], vv[8];
     ld8<GT>(grads, q, g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) g[k] *= gscale;
     if (MASTER) ld8<float>(master, q, th);
     else ld8<PT>(params, q, th);
     ld8<float>(m, q, mm);
@@ -433,14 +457,14 @@ __global__ __launch_bounds__(256) void k_adamw_vec8(PT* __restrict__ params,
   if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
     const int64_t i = (n8 << 3) + threadIdx.x;
     adamw_one<PT, GT, MASTER>(params, master, grads, m, v, i, b1, b2, eps, lr_bc1, rsqrt_bc2,
-                              decay);
+                              decay, gscale);
   }
 }
 
 template <typename PT, typename GT, bool MASTER>
 hipError_t adamw_dispatch(void* params, float* master, const void* grads, float* m, float* v,
                           int64_t n, float b1, float b2, float eps, float lr_bc1,
-                          float rsqrt_bc2, float decay, hipStream_t s) {
+                          float rsqrt_bc2, float decay, const ClipState* clip, hipStream_t s) {
   PT* p = static_cast<PT*>(params);
   const GT* g = static_cast<const GT*>(grads);
   const bool vec = aligned(p, 8 * sizeof(PT)) && aligned(g, 8 * sizeof(GT)) &&
@@ -452,11 +476,11 @@ hipError_t adamw_dispatch(void* params, float* master, const void* grads, float*
   if (vec)
     hipLaunchKernelGGL((k_adamw_vec8<PT, GT, MASTER>), dim3(static_cast<unsigned>(blocks)),
                        dim3(256), 0, s, p, master, g, m, v, n, b1, b2, eps, lr_bc1, rsqrt_bc2,
-                       decay);
+                       decay, clip);
   else
     hipLaunchKernelGGL((k_adamw_scalar<PT, GT, MASTER>), dim3(static_cast<unsigned>(blocks)),
                        dim3(256), 0, s, p, master, g, m, v, n, b1, b2, eps, lr_bc1, rsqrt_bc2,
-                       decay);
+                       decay, clip);
   return hipGetLastError();
 }
 
@@ -466,14 +490,15 @@ hipError_t adamw_dispatch(void* params, float* master, const void* grads, float*
 
 hipError_t launch_momentum(const MatDev* mats, const Item* items, int n_items, int grad_dtype,
                            int ns_dtype, const void* grads, float* mom, void* ws,
-                           float* partials, float mu, int nesterov, hipStream_t s) {
+                           float* partials, float mu, int nesterov, const ClipState* clip,
+                           hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items), block(256);
   const int al = aligned(grads, 4 * (grad_dtype == 1 ? 2 : 4)) && aligned(mom, 16);
 #define MUON_K1(GT, UT)                                                                   \
   hipLaunchKernelGGL((k_momentum<GT, UT>), grid, block, 0, s, mats, items,                \
                      static_cast<const GT*>(grads), mom, static_cast<UT*>(ws), partials, mu, \
-                     nesterov, al)
+                     nesterov, al, clip)
   if (grad_dtype == 1 && ns_dtype == 1) MUON_K1(uint16_t, uint16_t);
   else if (grad_dtype == 1 && ns_dtype == 0) MUON_K1(uint16_t, float);
   else if (grad_dtype == 0 && ns_dtype == 1) MUON_K1(float, uint16_t);
@@ -494,7 +519,8 @@ hipError_t launch_norm_finalize(const MatDev* mats, int mat_begin, int n_mats,
 hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int param_dtype,
                         int ns_dtype, void* params, const void* ws, const float* inv,
                         float o_scale_by_inv, int x_final, float lr, float wd, int scale_mode,
-                        float rms_target, float* out_update, hipStream_t s) {
+                        float rms_target, float* out_update, const ClipState* clip,
+                        hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items), block(256);
   const int use_inv = o_scale_by_inv != 0.0f;
@@ -503,7 +529,7 @@ hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int 
 #define MUON_K7(PT, UT)                                                                       \
   hipLaunchKernelGGL((k_apply<PT, UT>), grid, block, 0, s, mats, items, static_cast<PT*>(params), \
                      static_cast<const UT*>(ws), inv, use_inv, x_final, lr, wd, scale_mode,     \
-                     rms_target, out_update, al)
+                     rms_target, out_update, al, clip)
   if (param_dtype == 1 && ns_dtype == 1) MUON_K7(uint16_t, uint16_t);
   else if (param_dtype == 1 && ns_dtype == 0) MUON_K7(uint16_t, float);
   else if (param_dtype == 0 && ns_dtype == 1) MUON_K7(float, uint16_t);
@@ -527,13 +553,13 @@ hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int
 hipError_t launch_adamw(void* params, int param_dtype, float* master, const void* grads,
                         int grad_dtype, float* m, float* v, int64_t n, float lr, float beta1,
                         float beta2, float eps, float wd, float lr_bc1, float rsqrt_bc2,
-                        hipStream_t s) {
+                        const ClipState* clip, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const float decay = 1.0f - lr * wd;
   const bool ma = master != nullptr;
 #define MUON_K8(PT, GT, MA)                                                                 \
   return adamw_dispatch<PT, GT, MA>(params, master, grads, m, v, n, beta1, beta2, eps, lr_bc1, \
-                                    rsqrt_bc2, decay, s)
+                                    rsqrt_bc2, decay, clip, s)
   if (param_dtype == 1) {
     // bf16 parameters always come with a fp32 master (checked by the caller)
     if (grad_dtype == 1) MUON_K8(uint16_t, uint16_t, true);

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -348,6 +349,14 @@ int check_hparams(const muon_hparams_t* hp) {
 
 inline char* ws_bytes_ptr(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+static_assert(sizeof(muon_clip_state_t) == sizeof(muon::ClipState) &&
+                  offsetof(muon_clip_state_t, scale) == offsetof(muon::ClipState, scale) &&
+                  offsetof(muon_clip_state_t, skip) == offsetof(muon::ClipState, skip),
+              "muon_clip_state_t and its device view must agree");
+inline const muon::ClipState* clip_of(const muon_clip_state_t* c) {
+  return reinterpret_cast<const muon::ClipState*>(c);
+}
+
 muon::GemmArgs gemm_args(const muon_plan_t* p, const Wave& w, void* ws, const muon_hparams_t* hp,
                          int iter, const Item* items) {
   muon::GemmArgs g;
@@ -467,7 +476,7 @@ int muon_stage_momentum(const muon_plan_t* plan, int32_t wave, const void* grads
   hipError_t e = muon::launch_momentum(plan->d_mats, plan->d_k1 + w.k1_begin,
                                        static_cast<int>(w.k1_count), plan->grad_dtype,
                                        plan->ns_dtype, grads, momentum, workspace, partials,
-                                       hp->momentum, hp->nesterov, stream);
+                                       hp->momentum, hp->nesterov, clip_of(hp->clip), stream);
   if (e != hipSuccess) return hip_fail(e, "momentum kernel launch");
   e = muon::launch_norm_finalize(plan->d_mats, w.mat_begin, w.mat_end - w.mat_begin, partials,
                                  reinterpret_cast<float*>(ws_bytes_ptr(workspace, w.norm_off)),
@@ -510,7 +519,7 @@ int muon_stage_apply(const muon_plan_t* plan, int32_t wave, void* params, void* 
       plan->ns_dtype, params, workspace,
       reinterpret_cast<const float*>(ws_bytes_ptr(workspace, w.inv_off)),
       hp->ns_steps == 0 ? 1.0f : 0.0f, hp->ns_steps & 1, hp->lr, hp->weight_decay,
-      hp->scale_mode, hp->rms_target, out_update, stream);
+      hp->scale_mode, hp->rms_target, out_update, clip_of(hp->clip), stream);
   if (e != hipSuccess) return hip_fail(e, "apply kernel launch");
   return MUON_OK;
 }
@@ -596,8 +605,67 @@ int adamw_step(void* params, int32_t param_dtype, float* master, const void* gra
   const hipError_t e =
       muon::launch_adamw(params, param_dtype, master, grads, grad_dtype, exp_avg, exp_avg_sq, n,
                          hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, lr_bc1,
-                         rsqrt_bc2, stream);
+                         rsqrt_bc2, clip_of(hp->clip), stream);
   if (e != hipSuccess) return hip_fail(e, "AdamW kernel launch");
+  return MUON_OK;
+}
+
+size_t grad_norm_clip_workspace_size(int32_t n_bufs) {
+  return n_bufs > 0 ? static_cast<size_t>(n_bufs) * muon::kReduceBlocks * sizeof(double) : 0;
+}
+
+int grad_norm_clip(const muon_grad_buffer_t* bufs, int32_t n_bufs, float max_norm, float eps,
+                   void* workspace, size_t workspace_bytes, muon_clip_state_t* out,
+                   hipStream_t stream) {
+  if (out == nullptr) return fail(MUON_ERR_INVALID_ARG, "out is null");
+  if (n_bufs < 0 || (n_bufs > 0 && bufs == nullptr))
+    return fail(MUON_ERR_INVALID_ARG, "bad buffer list");
+  if (!std::isfinite(max_norm) || !std::isfinite(eps) || eps < 0.0f)
+    return fail(MUON_ERR_INVALID_ARG, "max_norm must be finite and eps finite and >= 0");
+  for (int32_t b = 0; b < n_bufs; ++b) {
+    if (bufs[b].n < 0) return fail(MUON_ERR_INVALID_ARG, "buffer " + std::to_string(b) + ": n < 0");
+    if (!dtype_ok(bufs[b].dtype))
+      return fail(MUON_ERR_BAD_DTYPE, "buffer " + std::to_string(b) + ": bad dtype");
+    if (bufs[b].n > 0 && bufs[b].ptr == nullptr)
+      return fail(MUON_ERR_INVALID_ARG, "buffer " + std::to_string(b) + " is null");
+  }
+  const size_t need = grad_norm_clip_workspace_size(n_bufs);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % alignof(double) != 0))
+    return fail(MUON_ERR_WORKSPACE_TOO_SMALL,
+                "grad_norm_clip needs " + std::to_string(need) + " bytes, 8-byte aligned");
+  double* partials = static_cast<double*>(workspace);
+  for (int32_t b = 0; b < n_bufs; ++b) {
+    const hipError_t e = muon::launch_sumsq(bufs[b].ptr, bufs[b].dtype, bufs[b].n,
+                                            partials + static_cast<size_t>(b) * muon::kReduceBlocks,
+                                            stream);
+    if (e != hipSuccess) return hip_fail(e, "sum-of-squares kernel launch");
+  }
+  const hipError_t e = muon::launch_clip_finalize(partials, n_bufs * muon::kReduceBlocks,
+                                                  max_norm, eps,
+                                                  reinterpret_cast<muon::ClipState*>(out), stream);
+  if (e != hipSuccess) return hip_fail(e, "clip kernel launch");
+  return MUON_OK;
+}
+
+size_t state_stats_workspace_size(void) {
+  return static_cast<size_t>(muon::kReduceBlocks) * muon::kStatsPartialBytes;
+}
+
+int state_stats(const float* x, int64_t n, void* workspace, size_t workspace_bytes,
+                muon_state_stats_t* out, hipStream_t stream) {
+  if (out == nullptr) return fail(MUON_ERR_INVALID_ARG, "out is null");
+  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && x == nullptr) return fail(MUON_ERR_INVALID_ARG, "x is null");
+  if (reinterpret_cast<uintptr_t>(out) % alignof(double) != 0)
+    return fail(MUON_ERR_INVALID_ARG, "out must be 8-byte aligned");
+  const size_t need = state_stats_workspace_size();
+  if (workspace == nullptr || workspace_bytes < need ||
+      reinterpret_cast<uintptr_t>(workspace) % alignof(double) != 0)
+    return fail(MUON_ERR_WORKSPACE_TOO_SMALL,
+                "state_stats needs " + std::to_string(need) + " bytes, 8-byte aligned");
+  const hipError_t e = muon::launch_state_stats(x, n, workspace, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "statistics kernel launch");
   return MUON_OK;
 }
 

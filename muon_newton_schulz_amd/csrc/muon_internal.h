@@ -55,11 +55,20 @@ struct GemmArgs {
   int32_t n_items;    // tile-list length (the persistent grid walks it)
 };
 
+// Device view of muon_clip_state_t (same layout): the gradient scale and
+// the skip flag of a guarded step.  A null pointer means scale 1, no skip.
+struct ClipState {
+  float norm;
+  float scale;
+  int32_t skip;
+  int32_t reserved;
+};
+
 // kernel launchers (defined in the .hip files)
 hipError_t launch_momentum(const MatDev* mats, const Item* items, int n_items,
                            int grad_dtype, int ns_dtype, const void* grads, float* mom,
                            void* ws, float* partials, float mu, int nesterov,
-                           hipStream_t s);
+                           const ClipState* clip, hipStream_t s);
 hipError_t launch_norm_finalize(const MatDev* mats, int mat_begin, int n_mats,
                                 const float* partials, float* norms, float* inv,
                                 float eps, hipStream_t s);
@@ -67,7 +76,7 @@ hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int 
                         int ns_dtype, void* params, const void* ws, const float* inv,
                         float o_scale_by_inv, int x_final, float lr, float wd,
                         int scale_mode, float rms_target, float* out_update,
-                        hipStream_t s);
+                        const ClipState* clip, hipStream_t s);
 hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int ns_dtype,
                          const void* ws, int x_idx, float* out, hipStream_t s);
 hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
@@ -75,7 +84,18 @@ hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
 hipError_t launch_adamw(void* params, int param_dtype, float* master, const void* grads,
                         int grad_dtype, float* m, float* v, int64_t n, float lr,
                         float beta1, float beta2, float eps, float wd, float lr_bc1,
-                        float rsqrt_bc2, hipStream_t s);
+                        float rsqrt_bc2, const ClipState* clip, hipStream_t s);
+// Global gradient norm: one launch per buffer writes kReduceBlocks fp64
+// partial sums of squares at partials + index * kReduceBlocks; the
+// finalize launch reduces n_bufs * kReduceBlocks partials in order.
+constexpr int kReduceBlocks = 1024;
+hipError_t launch_sumsq(const void* g, int dtype, int64_t n, double* partials, hipStream_t s);
+hipError_t launch_clip_finalize(const double* partials, int n_parts, float max_norm, float eps,
+                                ClipState* out, hipStream_t s);
+// State statistics: kReduceBlocks partials of kStatsPartialBytes each.
+constexpr int kStatsPartialBytes = 64;
+hipError_t launch_state_stats(const float* x, int64_t n, void* partials, void* out,
+                              hipStream_t s);
 
 // bf16 <-> fp32 (bf16 stored as its 16-bit pattern)
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

@@ -97,3 +97,45 @@ def test_adamw_validation_before_any_hip_call():
     assert _err(M.adamw_step, p32, None, p32, m, v, bad, 1, stream=0) == M.MUON_ERR_INVALID_ARG
     assert _err(M.adamw_step, p32, None, p32, m, torch.zeros(7), hp, 1, stream=0) == \
         M.MUON_ERR_INVALID_ARG
+
+
+def test_guard_entry_points_validate_before_any_hip_call():
+    L = M.lib()
+    P = ctypes.c_void_p
+    fake = P(4096)  # never dereferenced: every case fails validation first
+    bufs = (M.MuonGradBuffer * 2)(M.MuonGradBuffer(fake, 10, 1, 0), M.MuonGradBuffer(fake, 10, 7, 0))
+    ws_need = M.grad_norm_clip_workspace_size(2)
+    assert ws_need == 2 * 1024 * 8
+    assert M.grad_norm_clip_workspace_size(0) == 0
+    assert L.grad_norm_clip(bufs, 2, 1.0, 1e-6, fake, ws_need, fake, None) == M.MUON_ERR_BAD_DTYPE
+    bufs[1] = M.MuonGradBuffer(None, 10, 0, 0)
+    assert L.grad_norm_clip(bufs, 2, 1.0, 1e-6, fake, ws_need, fake, None) == M.MUON_ERR_INVALID_ARG
+    bufs[1] = M.MuonGradBuffer(None, -1, 0, 0)
+    assert L.grad_norm_clip(bufs, 2, 1.0, 1e-6, fake, ws_need, fake, None) == M.MUON_ERR_INVALID_ARG
+    bufs[1] = M.MuonGradBuffer(None, 0, 0, 0)  # empty buffers may be null
+    assert L.grad_norm_clip(bufs, 2, 1.0, 1e-6, fake, ws_need - 8, fake, None) == \
+        M.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert L.grad_norm_clip(bufs, 2, 1.0, 1e-6, fake, ws_need, None, None) == M.MUON_ERR_INVALID_ARG
+    assert L.grad_norm_clip(bufs, 2, float("nan"), 1e-6, fake, ws_need, fake, None) == \
+        M.MUON_ERR_INVALID_ARG
+    assert L.grad_norm_clip(bufs, 2, 1.0, -1.0, fake, ws_need, fake, None) == M.MUON_ERR_INVALID_ARG
+    assert L.grad_norm_clip(None, 1, 1.0, 1e-6, fake, ws_need, fake, None) == M.MUON_ERR_INVALID_ARG
+    s_need = M.state_stats_workspace_size()
+    assert s_need == 1024 * 64
+    assert L.state_stats(fake, 10, fake, s_need, None, None) == M.MUON_ERR_INVALID_ARG
+    assert L.state_stats(fake, -1, fake, s_need, fake, None) == M.MUON_ERR_INVALID_ARG
+    assert L.state_stats(None, 10, fake, s_need, fake, None) == M.MUON_ERR_INVALID_ARG
+    assert L.state_stats(fake, 10, fake, s_need - 1, fake, None) == M.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert L.state_stats(fake, 10, P(4097), s_need, fake, None) == M.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert L.state_stats(fake, 10, fake, s_need, P(4100), None) == M.MUON_ERR_INVALID_ARG
+
+
+def test_hparam_structs_carry_the_clip_pointer():
+    # the binding's structs mirror include/muon.h: the clip pointer is last
+    assert [f for f, _ in M.MuonHParamsC._fields_][-1] == "clip"
+    assert [f for f, _ in M.AdamWHParamsC._fields_][-1] == "clip"
+    assert ctypes.sizeof(M.MuonClipState) == 16
+    assert ctypes.sizeof(M.MuonStateStats) == 56
+    assert ctypes.sizeof(M.MuonGradBuffer) == 24
+    h = M._hp(M.MuonHParamsC(0.02, 0.1, 0.95, 1, 1.5, -0.5, 0.0, 5, 1e-7, 0, 0.2))
+    assert h.clip is None
