@@ -237,6 +237,38 @@ def main():
     copy_gbps = 5 * 2 * (1 << 30) / (a.elapsed_time(b_) * 1e-3) / 1e9
     del src, dst
 
+    # ---- the safety net around the step (outside the timed step): the
+    # global gradient norm behind clipping and the step guard, over every
+    # gradient of the workload, and the statistics of the Muon momentum
+    grad_bufs = [inp.grads] + [a.grad for a in adam]
+    grad_bytes = sum(g.numel() * g.element_size() for g in grad_bufs)
+    clip_ws = torch.empty(max(8, M.grad_norm_clip_workspace_size(len(grad_bufs))),
+                          dtype=torch.uint8, device=dev)
+    clip_out = torch.zeros(16, dtype=torch.uint8, device=dev)
+    stats_ws = torch.empty(M.state_stats_workspace_size(), dtype=torch.uint8, device=dev)
+    stats_out = torch.zeros(64, dtype=torch.uint8, device=dev)
+
+    def time_launch(fn, reps=5):
+        fn()
+        a, b_ = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / reps
+
+    clip_ms = time_launch(lambda: M.grad_norm_clip(grad_bufs, 1.0, out=clip_out,
+                                                   workspace=clip_ws))
+    stats_ms = time_launch(lambda: M.state_stats(inp.momentum, out=stats_out,
+                                                 workspace=stats_ws))
+    guard = {
+        "grad_norm_clip": {"ms": clip_ms, "bytes": grad_bytes,
+                           "gbps": grad_bytes / (clip_ms * 1e-3) / 1e9},
+        "state_stats_momentum": {"ms": stats_ms, "bytes": inp.momentum.numel() * 4,
+                                 "gbps": inp.momentum.numel() * 4 / (stats_ms * 1e-3) / 1e9},
+    }
+
     ceiling = mfma_ceiling()
 
     # ---- algorithmic work
@@ -321,6 +353,9 @@ def main():
             "plain_copy_1GiB": copy_gbps,
         },
         "wall_s_timed_region": wall1 - wall0,
+        # optimizer-tutorial 5.4 safety net, timed separately from the step
+        # (algorithmic bytes: every gradient, or the momentum, read once)
+        "guard": guard,
     }
     if not args.no_cpu_baseline:
         # first layer of the stack: 4 square + 3 rectangular matrices
