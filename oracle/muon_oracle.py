@@ -48,6 +48,12 @@ R8  AdamW as printed in [OPT] 2.3 and 3.1 with the extraction damage undone:
     eps outside the square root, t starting at 1.
 R9  Mixed precision ([OPT] 3.3): the update runs on the fp32 master copy and
     the bf16 parameter is the round-to-nearest-even cast of that fp32 value.
+R13 Compressed AdamW states ([OPT] 2.4 lists 8-bit AdamW states; 3.3: v
+    tolerates FP16 or 8-bit storage, m is more sensitive, so v is compressed
+    first): a step reads m and v from their storage type, computes in full
+    precision, and stores m as fp32 or bf16 and v as fp32, bf16 or fp16
+    (round to nearest even).  The pages fix no 8-bit encoding; none is
+    defined here.
 
 Parity status: every function below is pinned by tests/test_oracle_pins.py
 (closed forms, SVD spectral calculus, invariants, library bf16 casts).
@@ -93,9 +99,21 @@ def bf16_round(x) -> np.ndarray:
     return out
 
 
+def fp16_round(x) -> np.ndarray:
+    """Round to IEEE binary16 (round to nearest even; subnormals kept;
+    beyond the largest finite value, +-inf).  As for bf16, the input is first
+    rounded to fp32, the precision the step computes in.  Returned as
+    float64 holding the fp16 value exactly."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float16).astype(
+            np.float64)
+
+
 def round_to(x, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_round(x)
+    if dtype == "fp16":
+        return fp16_round(x)
     if dtype == "fp32":
         return fp32_round(x)
     if dtype == "fp64":
@@ -292,23 +310,34 @@ def adamw_math(theta: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray,
 
 def adamw_step_stored(param: np.ndarray, master: np.ndarray | None,
                       g: np.ndarray, m: np.ndarray, v: np.ndarray,
-                      hp: AdamWHP, t: int, param_dtype: str, grad_scale: float = 1.0
+                      hp: AdamWHP, t: int, param_dtype: str, grad_scale: float = 1.0,
+                      m_dtype: str = "fp32", v_dtype: str = "fp32"
                       ) -> Tuple[np.ndarray, np.ndarray | None, np.ndarray, np.ndarray]:
-    """AdamW step with storage rounding ([OPT] 3.3, reading R9).
+    """AdamW step with storage rounding ([OPT] 3.3, readings R9, R13).
 
     With a master copy: the fp32 master is updated and the parameter becomes
     the bf16 (or fp32) cast of the new fp32 master.  Without one: the
-    parameter itself must be fp32 and is updated in place.
+    parameter itself must be fp32 and is updated in place.  m and v are
+    stored as ``m_dtype`` / ``v_dtype`` (their inputs are the stored values
+    of the previous step).
     Returns (param_new, master_new or None, m_new, v_new).
     """
     theta = master if master is not None else param
     th, m_new, v_new = adamw_math(theta, g, m, v, hp, t, grad_scale)
     th32 = fp32_round(th)
+    m_st, v_st = round_to(m_new, m_dtype), round_to(v_new, v_dtype)
     if master is not None:
-        return round_to(th32, param_dtype), th32, fp32_round(m_new), fp32_round(v_new)
+        return round_to(th32, param_dtype), th32, m_st, v_st
     if param_dtype != "fp32":
         raise ValueError("without a master copy the parameter must be fp32")
-    return th32, None, fp32_round(m_new), fp32_round(v_new)
+    return th32, None, m_st, v_st
+
+
+def adamw_state_bytes_per_param(m_dtype: str = "fp32", v_dtype: str = "fp32") -> int:
+    """[OPT] 2.4: Adam keeps two states per parameter, fp32 in the standard
+    implementation (8 bytes); compressed states take their storage size."""
+    size = {"fp32": 4, "bf16": 2, "fp16": 2}
+    return size[m_dtype] + size[v_dtype]
 
 
 def muon_state_bytes_per_param() -> int:
@@ -317,7 +346,8 @@ def muon_state_bytes_per_param() -> int:
 
 
 __all__: List[str] = [
-    "AdamWHP", "MuonHP", "adamw_math", "adamw_step_stored", "bf16_round",
+    "AdamWHP", "MuonHP", "adamw_math", "adamw_state_bytes_per_param", "adamw_step_stored",
+    "bf16_round", "fp16_round",
     "ema_momentum", "fp32_round", "frobenius_normalise", "muon_matrix_math",
     "muon_step_flat", "nesterov_lookahead", "newton_schulz", "ns_flops",
     "ns_iteration", "round_to", "update_scale",
