@@ -58,6 +58,7 @@ extern "C" {
 /* ---- element types ---------------------------------------------------- */
 #define MUON_DTYPE_FP32 0
 #define MUON_DTYPE_BF16 1
+#define MUON_DTYPE_FP16 2 /* IEEE binary16: AdamW second moment only */
 
 /* One matrix of the flat buffer ([K2] 2.2): elements
  * [offset, offset + rows*cols) of the flat params / grads / momentum
@@ -219,6 +220,21 @@ int muon_stage_export_norms(const muon_plan_t* plan, int32_t wave, const void* w
 int adamw_step(void* params, int32_t param_dtype, float* master, const void* grads,
                int32_t grad_dtype, float* exp_avg, float* exp_avg_sq, int64_t n,
                const adamw_hparams_t* hp, int64_t step, hipStream_t stream);
+
+/* adamw_step with compressed optimizer states ([OPT] 2.4: 8-bit AdamW
+ * states; 3.3: v tolerates 16-bit or 8-bit storage before m does):
+ *   exp_avg_dtype    MUON_DTYPE_FP32 or MUON_DTYPE_BF16
+ *   exp_avg_sq_dtype MUON_DTYPE_FP32, MUON_DTYPE_BF16 or MUON_DTYPE_FP16
+ * The step reads m and v from their storage, computes in fp32 and stores
+ * them rounded to nearest even.  fp16 keeps 10 fraction bits but its
+ * smallest subnormal is 2^-24: (1 - beta2) g^2 below 2^-25 is stored as
+ * 0, which makes later updates m_hat / eps large for small gradients;
+ * bf16 keeps fp32's range with 7 fraction bits.  adamw_step(...) equals
+ * adamw_step_ex(..., MUON_DTYPE_FP32, ..., MUON_DTYPE_FP32, ...). */
+int adamw_step_ex(void* params, int32_t param_dtype, float* master, const void* grads,
+                  int32_t grad_dtype, void* exp_avg, int32_t exp_avg_dtype, void* exp_avg_sq,
+                  int32_t exp_avg_sq_dtype, int64_t n, const adamw_hparams_t* hp, int64_t step,
+                  hipStream_t stream);
 
 /* ---- gradient clipping, step guard, state statistics ([OPT] 5.4) ------ */
 

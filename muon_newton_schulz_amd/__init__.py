@@ -28,11 +28,13 @@ MUON_ERR_UNSUPPORTED = -7
 
 MUON_DTYPE_FP32 = 0
 MUON_DTYPE_BF16 = 1
+MUON_DTYPE_FP16 = 2
 
 EXPORTED = [
     "muon_workspace_size", "muon_plan_create", "muon_plan_destroy", "muon_plan_get_info",
     "muon_step", "muon_stage_momentum", "muon_stage_ns_phase", "muon_stage_apply",
-    "muon_stage_export_x", "muon_stage_export_norms", "adamw_step", "muon_status_string",
+    "muon_stage_export_x", "muon_stage_export_norms", "adamw_step", "adamw_step_ex",
+    "muon_status_string",
     "muon_last_error", "grad_norm_clip_workspace_size", "grad_norm_clip",
     "state_stats_workspace_size", "state_stats",
 ]
@@ -117,6 +119,8 @@ def lib() -> ctypes.CDLL:
     L.muon_stage_export_x.argtypes = [P, I32, P, SZ, I32, P, P]
     L.muon_stage_export_norms.argtypes = [P, I32, P, SZ, P, P]
     L.adamw_step.argtypes = [P, I32, P, P, I32, P, P, I64, ctypes.POINTER(AdamWHParamsC), I64, P]
+    L.adamw_step_ex.argtypes = [P, I32, P, P, I32, P, I32, P, I32, I64,
+                                ctypes.POINTER(AdamWHParamsC), I64, P]
     L.grad_norm_clip_workspace_size.argtypes = [I32]
     L.grad_norm_clip_workspace_size.restype = SZ
     L.grad_norm_clip.argtypes = [ctypes.POINTER(MuonGradBuffer), I32, ctypes.c_float,
@@ -154,8 +158,9 @@ def muon_last_error() -> str:
 
 def dtype_code(dt) -> int:
     import torch
-    table = {"fp32": MUON_DTYPE_FP32, "bf16": MUON_DTYPE_BF16,
-             torch.float32: MUON_DTYPE_FP32, torch.bfloat16: MUON_DTYPE_BF16}
+    table = {"fp32": MUON_DTYPE_FP32, "bf16": MUON_DTYPE_BF16, "fp16": MUON_DTYPE_FP16,
+             torch.float32: MUON_DTYPE_FP32, torch.bfloat16: MUON_DTYPE_BF16,
+             torch.float16: MUON_DTYPE_FP16}
     if dt not in table:
         raise MuonError(MUON_ERR_BAD_DTYPE, f"unsupported dtype {dt}")
     return table[dt]
@@ -314,16 +319,19 @@ def muon_stage_export_norms(plan: MuonPlan, wave: int, workspace, out, stream=No
 def adamw_step(params, master, grads, exp_avg, exp_avg_sq, hp, step: int, stream=None,
                clip=None) -> None:
     """params/grads may be bf16 or fp32 tensors; master (fp32) may be None;
-    clip: optional device clip state from grad_norm_clip."""
+    exp_avg may be fp32 or bf16 and exp_avg_sq fp32, bf16 or fp16 (the
+    compressed states of adamw_step_ex); clip: optional device clip state
+    from grad_norm_clip."""
     n = params.numel()
     for name, t in (("grads", grads), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq),
                     ("master", master)):
         if t is not None and t.numel() != n:
             raise MuonError(MUON_ERR_INVALID_ARG, f"{name} has {t.numel()} elements, expected {n}")
     h = _ahp(hp, clip)
-    _check(lib().adamw_step(_ptr(params), dtype_code(params.dtype), _ptr(master), _ptr(grads),
-                            dtype_code(grads.dtype), _ptr(exp_avg), _ptr(exp_avg_sq), n,
-                            ctypes.byref(h), int(step), _stream(stream)))
+    _check(lib().adamw_step_ex(_ptr(params), dtype_code(params.dtype), _ptr(master), _ptr(grads),
+                               dtype_code(grads.dtype), _ptr(exp_avg), dtype_code(exp_avg.dtype),
+                               _ptr(exp_avg_sq), dtype_code(exp_avg_sq.dtype), n,
+                               ctypes.byref(h), int(step), _stream(stream)))
 
 
 # ------------------------------------------ clipping, step guard, statistics

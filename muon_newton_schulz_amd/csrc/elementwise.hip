@@ -43,6 +43,15 @@ template <> struct Elem<uint16_t> {
     p[i] = f32_to_bf16(v);
   }
 };
+// IEEE binary16 (AdamW second moment only); the cast rounds to nearest even
+template <> struct Elem<_Float16> {
+  static __device__ __forceinline__ float ld(const _Float16* p, int64_t i) {
+    return static_cast<float>(p[i]);
+  }
+  static __device__ __forceinline__ void st(_Float16* p, int64_t i, float v) {
+    p[i] = static_cast<_Float16>(v);
+  }
+};
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -338,30 +347,36 @@ __global__ __launch_bounds__(256) void k_export(const MatDev* __restrict__ mats,
 }
 
 // ---------------------------------------------------------------- AdamW
+//
+// Template parameters: PT parameter storage, GT gradient storage, MT / VT
+// storage of the first / second moment (float; uint16_t = bf16; _Float16
+// for the second moment), MASTER: a fp32 master copy is updated and the
+// parameter receives its cast.  A step reads the states from their
+// storage, computes in fp32 and stores them rounded to nearest even.
 
-template <typename PT, typename GT, bool MASTER>
-__device__ __forceinline__ void adamw_one(PT* params, float* master, const GT* grads, float* m,
-                                          float* v, int64_t i, float b1, float b2, float eps,
+template <typename PT, typename GT, typename MT, typename VT, bool MASTER>
+__device__ __forceinline__ void adamw_one(PT* params, float* master, const GT* grads, MT* m,
+                                          VT* v, int64_t i, float b1, float b2, float eps,
                                           float lr_bc1, float rsqrt_bc2, float decay,
                                           float gscale) {
   const float g = gscale * Elem<GT>::ld(grads, i);
   const float th = MASTER ? master[i] : Elem<PT>::ld(params, i);
-  const float mm = b1 * m[i] + (1.0f - b1) * g;
-  const float vv = b2 * v[i] + (1.0f - b2) * g * g;
+  const float mm = b1 * Elem<MT>::ld(m, i) + (1.0f - b1) * g;
+  const float vv = b2 * Elem<VT>::ld(v, i) + (1.0f - b2) * g * g;
   const float den = sqrtf(vv) * rsqrt_bc2 + eps;
   const float nt = th * decay - lr_bc1 * (mm / den);
-  m[i] = mm;
-  v[i] = vv;
+  Elem<MT>::st(m, i, mm);
+  Elem<VT>::st(v, i, vv);
   if (MASTER) master[i] = nt;
   Elem<PT>::st(params, i, nt);
 }
 
 // Scalar grid-stride variant: any alignment.
-template <typename PT, typename GT, bool MASTER>
+template <typename PT, typename GT, typename MT, typename VT, bool MASTER>
 __global__ __launch_bounds__(256) void k_adamw_scalar(PT* __restrict__ params,
                                                       float* __restrict__ master,
                                                       const GT* __restrict__ grads,
-                                                      float* __restrict__ m, float* __restrict__ v,
+                                                      MT* __restrict__ m, VT* __restrict__ v,
                                                       int64_t n, float b1, float b2, float eps,
                                                       float lr_bc1, float rsqrt_bc2,
                                                       float decay,
@@ -374,14 +389,15 @@ __global__ __launch_bounds__(256) void k_adamw_scalar(PT* __restrict__ params,
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += stride)
-    adamw_one<PT, GT, MASTER>(params, master, grads, m, v, i, b1, b2, eps, lr_bc1, rsqrt_bc2,
-                              decay, gscale);
+    adamw_one<PT, GT, MT, VT, MASTER>(params, master, grads, m, v, i, b1, b2, eps, lr_bc1,
+                                      rsqrt_bc2, decay, gscale);
 }
 
-// 8 consecutive elements per thread and iteration: bf16 vectors are 16
+// 8 consecutive elements per thread and iteration: 16-bit vectors are 16
 // bytes, fp32 vectors two 16-byte loads.  Every pointer is aligned to 8
 // elements (checked on the host); the tail of n % 8 elements is done by the
 // first threads of block 0.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 template <typename T>
 __device__ __forceinline__ void ld8(const T* p, int64_t q, float* o);
 template <>
@@ -400,6 +416,12 @@ __device__ __forceinline__ void ld8<uint16_t>(const uint16_t* p, int64_t q, floa
     o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
   }
 }
+template <>
+__device__ __forceinline__ void ld8<_Float16>(const _Float16* p, int64_t q, float* o) {
+  const f16x8_t h = reinterpret_cast<const f16x8_t*>(p)[q];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = static_cast<float>(h[k]);
+}
 template <typename T>
 __device__ __forceinline__ void st8(T* p, int64_t q, const float* o);
 template <>
@@ -416,12 +438,19 @@ __device__ __forceinline__ void st8<uint16_t>(uint16_t* p, int64_t q, const floa
            (static_cast<uint32_t>(f32_to_bf16(o[2 * k + 1])) << 16);
   reinterpret_cast<uint4*>(p)[q] = make_uint4(w[0], w[1], w[2], w[3]);
 }
+template <>
+__device__ __forceinline__ void st8<_Float16>(_Float16* p, int64_t q, const float* o) {
+  f16x8_t h;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h[k] = static_cast<_Float16>(o[k]);
+  reinterpret_cast<f16x8_t*>(p)[q] = h;
+}
 
-template <typename PT, typename GT, bool MASTER>
+template <typename PT, typename GT, typename MT, typename VT, bool MASTER>
 __global__ __launch_bounds__(256) void k_adamw_vec8(PT* __restrict__ params,
                                                     float* __restrict__ master,
                                                     const GT* __restrict__ grads,
-                                                    float* __restrict__ m, float* __restrict__ v,
+                                                    MT* __restrict__ m, VT* __restrict__ v,
                                                     int64_t n, float b1, float b2, float eps,
                                                     float lr_bc1, float rsqrt_bc2, float decay,
                                                     const ClipState* __restrict__ clip) {
@@ -440,8 +469,8 @@ __global__ __launch_bounds__(256) void k_adamw_vec8(PT* __restrict__ params,
     for (int k = 0; k < 8; ++k) g[k] *= gscale;
     if (MASTER) ld8<float>(master, q, th);
     else ld8<PT>(params, q, th);
-    ld8<float>(m, q, mm);
-    ld8<float>(v, q, vv);
+    ld8<MT>(m, q, mm);
+    ld8<VT>(v, q, vv);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       mm[k] = b1 * mm[k] + (1.0f - b1) * g[k];
@@ -449,39 +478,61 @@ __global__ __launch_bounds__(256) void k_adamw_vec8(PT* __restrict__ params,
       const float den = sqrtf(vv[k]) * rsqrt_bc2 + eps;
       th[k] = th[k] * decay - lr_bc1 * (mm[k] / den);
     }
-    st8<float>(m, q, mm);
-    st8<float>(v, q, vv);
+    st8<MT>(m, q, mm);
+    st8<VT>(v, q, vv);
     if (MASTER) st8<float>(master, q, th);
     st8<PT>(params, q, th);
   }
   if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
     const int64_t i = (n8 << 3) + threadIdx.x;
-    adamw_one<PT, GT, MASTER>(params, master, grads, m, v, i, b1, b2, eps, lr_bc1, rsqrt_bc2,
-                              decay, gscale);
+    adamw_one<PT, GT, MT, VT, MASTER>(params, master, grads, m, v, i, b1, b2, eps, lr_bc1,
+                                      rsqrt_bc2, decay, gscale);
   }
 }
 
-template <typename PT, typename GT, bool MASTER>
-hipError_t adamw_dispatch(void* params, float* master, const void* grads, float* m, float* v,
+template <typename PT, typename GT, typename MT, typename VT, bool MASTER>
+hipError_t adamw_dispatch(void* params, float* master, const void* grads, void* mv, void* vv,
                           int64_t n, float b1, float b2, float eps, float lr_bc1,
                           float rsqrt_bc2, float decay, const ClipState* clip, hipStream_t s) {
   PT* p = static_cast<PT*>(params);
   const GT* g = static_cast<const GT*>(grads);
+  MT* m = static_cast<MT*>(mv);
+  VT* v = static_cast<VT*>(vv);
   const bool vec = aligned(p, 8 * sizeof(PT)) && aligned(g, 8 * sizeof(GT)) &&
-                   aligned(m, 32) && aligned(v, 32) && (!MASTER || aligned(master, 32));
+                   aligned(m, 8 * sizeof(MT)) && aligned(v, 8 * sizeof(VT)) &&
+                   (!MASTER || aligned(master, 32));
   const int64_t work = vec ? (n >> 3) : n;
   int64_t blocks = (work + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   if (vec)
-    hipLaunchKernelGGL((k_adamw_vec8<PT, GT, MASTER>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, s, p, master, g, m, v, n, b1, b2, eps, lr_bc1, rsqrt_bc2,
-                       decay, clip);
+    hipLaunchKernelGGL((k_adamw_vec8<PT, GT, MT, VT, MASTER>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, master, g, m, v,
+                       n, b1, b2, eps, lr_bc1, rsqrt_bc2, decay, clip);
   else
-    hipLaunchKernelGGL((k_adamw_scalar<PT, GT, MASTER>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, s, p, master, g, m, v, n, b1, b2, eps, lr_bc1, rsqrt_bc2,
-                       decay, clip);
+    hipLaunchKernelGGL((k_adamw_scalar<PT, GT, MT, VT, MASTER>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, master, g, m, v,
+                       n, b1, b2, eps, lr_bc1, rsqrt_bc2, decay, clip);
   return hipGetLastError();
+}
+
+// state storage: m fp32 / bf16, v fp32 / bf16 / fp16
+template <typename PT, typename GT, bool MASTER>
+hipError_t adamw_states(int m_dtype, int v_dtype, void* params, float* master, const void* grads,
+                        void* m, void* v, int64_t n, float b1, float b2, float eps, float lr_bc1,
+                        float rsqrt_bc2, float decay, const ClipState* clip, hipStream_t s) {
+#define MUON_K8S(MT, VT)                                                                      \
+  return adamw_dispatch<PT, GT, MT, VT, MASTER>(params, master, grads, m, v, n, b1, b2, eps,  \
+                                                lr_bc1, rsqrt_bc2, decay, clip, s)
+  if (m_dtype == 1) {
+    if (v_dtype == 2) MUON_K8S(uint16_t, _Float16);
+    if (v_dtype == 1) MUON_K8S(uint16_t, uint16_t);
+    MUON_K8S(uint16_t, float);
+  }
+  if (v_dtype == 2) MUON_K8S(float, _Float16);
+  if (v_dtype == 1) MUON_K8S(float, uint16_t);
+  MUON_K8S(float, float);
+#undef MUON_K8S
 }
 
 }  // namespace
@@ -551,15 +602,15 @@ hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int
 }
 
 hipError_t launch_adamw(void* params, int param_dtype, float* master, const void* grads,
-                        int grad_dtype, float* m, float* v, int64_t n, float lr, float beta1,
-                        float beta2, float eps, float wd, float lr_bc1, float rsqrt_bc2,
-                        const ClipState* clip, hipStream_t s) {
+                        int grad_dtype, void* m, int m_dtype, void* v, int v_dtype, int64_t n,
+                        float lr, float beta1, float beta2, float eps, float wd, float lr_bc1,
+                        float rsqrt_bc2, const ClipState* clip, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const float decay = 1.0f - lr * wd;
   const bool ma = master != nullptr;
-#define MUON_K8(PT, GT, MA)                                                                 \
-  return adamw_dispatch<PT, GT, MA>(params, master, grads, m, v, n, beta1, beta2, eps, lr_bc1, \
-                                    rsqrt_bc2, decay, clip, s)
+#define MUON_K8(PT, GT, MA)                                                                    \
+  return adamw_states<PT, GT, MA>(m_dtype, v_dtype, params, master, grads, m, v, n, beta1,     \
+                                  beta2, eps, lr_bc1, rsqrt_bc2, decay, clip, s)
   if (param_dtype == 1) {
     // bf16 parameters always come with a fp32 master (checked by the caller)
     if (grad_dtype == 1) MUON_K8(uint16_t, uint16_t, true);

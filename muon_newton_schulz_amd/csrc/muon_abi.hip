@@ -579,12 +579,17 @@ int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* m
   return MUON_OK;
 }
 
-int adamw_step(void* params, int32_t param_dtype, float* master, const void* grads,
-               int32_t grad_dtype, float* exp_avg, float* exp_avg_sq, int64_t n,
-               const adamw_hparams_t* hp, int64_t step, hipStream_t stream) {
+int adamw_step_ex(void* params, int32_t param_dtype, float* master, const void* grads,
+                  int32_t grad_dtype, void* exp_avg, int32_t exp_avg_dtype, void* exp_avg_sq,
+                  int32_t exp_avg_sq_dtype, int64_t n, const adamw_hparams_t* hp, int64_t step,
+                  hipStream_t stream) {
   if (hp == nullptr) return fail(MUON_ERR_INVALID_ARG, "hparams is null");
   if (!dtype_ok(param_dtype) || !dtype_ok(grad_dtype))
     return fail(MUON_ERR_BAD_DTYPE, "dtype must be MUON_DTYPE_FP32 or MUON_DTYPE_BF16");
+  if (!dtype_ok(exp_avg_dtype))
+    return fail(MUON_ERR_BAD_DTYPE, "exp_avg must be MUON_DTYPE_FP32 or MUON_DTYPE_BF16");
+  if (!dtype_ok(exp_avg_sq_dtype) && exp_avg_sq_dtype != MUON_DTYPE_FP16)
+    return fail(MUON_ERR_BAD_DTYPE, "exp_avg_sq must be MUON_DTYPE_FP32, _BF16 or _FP16");
   if (param_dtype == MUON_DTYPE_BF16 && master == nullptr)
     return fail(MUON_ERR_INVALID_ARG, "bf16 parameters need a fp32 master copy");
   if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n < 0");
@@ -602,12 +607,19 @@ int adamw_step(void* params, int32_t param_dtype, float* master, const void* gra
   const double bc2 = 1.0 - std::pow(static_cast<double>(hp->beta2), static_cast<double>(step));
   const float lr_bc1 = static_cast<float>(static_cast<double>(hp->lr) / bc1);
   const float rsqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
-  const hipError_t e =
-      muon::launch_adamw(params, param_dtype, master, grads, grad_dtype, exp_avg, exp_avg_sq, n,
-                         hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, lr_bc1,
-                         rsqrt_bc2, clip_of(hp->clip), stream);
+  const hipError_t e = muon::launch_adamw(
+      params, param_dtype, master, grads, grad_dtype, exp_avg, exp_avg_dtype, exp_avg_sq,
+      exp_avg_sq_dtype, n, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, lr_bc1,
+      rsqrt_bc2, clip_of(hp->clip), stream);
   if (e != hipSuccess) return hip_fail(e, "AdamW kernel launch");
   return MUON_OK;
+}
+
+int adamw_step(void* params, int32_t param_dtype, float* master, const void* grads,
+               int32_t grad_dtype, float* exp_avg, float* exp_avg_sq, int64_t n,
+               const adamw_hparams_t* hp, int64_t step, hipStream_t stream) {
+  return adamw_step_ex(params, param_dtype, master, grads, grad_dtype, exp_avg, MUON_DTYPE_FP32,
+                       exp_avg_sq, MUON_DTYPE_FP32, n, hp, step, stream);
 }
 
 size_t grad_norm_clip_workspace_size(int32_t n_bufs) {

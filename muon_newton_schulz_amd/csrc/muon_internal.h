@@ -81,9 +81,10 @@ hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int
                          const void* ws, int x_idx, float* out, hipStream_t s);
 hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
                            const GemmArgs& args, hipStream_t s);
+// m_dtype: 0 fp32, 1 bf16; v_dtype: 0 fp32, 1 bf16, 2 fp16
 hipError_t launch_adamw(void* params, int param_dtype, float* master, const void* grads,
-                        int grad_dtype, float* m, float* v, int64_t n, float lr,
-                        float beta1, float beta2, float eps, float wd, float lr_bc1,
+                        int grad_dtype, void* m, int m_dtype, void* v, int v_dtype, int64_t n,
+                        float lr, float beta1, float beta2, float eps, float wd, float lr_bc1,
                         float rsqrt_bc2, const ClipState* clip, hipStream_t s);
 // Global gradient norm: one launch per buffer writes kReduceBlocks fp64
 // partial sums of squares at partials + index * kReduceBlocks; the

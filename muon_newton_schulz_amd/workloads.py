@@ -329,9 +329,11 @@ def apply_bytes_per_param(param_dtype: str, ns_dtype: str = "bf16") -> int:
     return 2 * DTYPE_BYTES[param_dtype] + DTYPE_BYTES[ns_dtype]
 
 
-def adamw_bytes_per_param(param_dtype: str, grad_dtype: str, master: bool) -> int:
+def adamw_bytes_per_param(param_dtype: str, grad_dtype: str, master: bool,
+                          m_dtype: str = "fp32", v_dtype: str = "fp32") -> int:
     """Read g, theta (master or param), m, v; write theta, m, v (+ param)."""
-    b = DTYPE_BYTES[grad_dtype] + 3 * 4 + 3 * 4
+    theta = 4 if master else DTYPE_BYTES[param_dtype]
+    b = DTYPE_BYTES[grad_dtype] + 2 * (theta + DTYPE_BYTES[m_dtype] + DTYPE_BYTES[v_dtype])
     if master:
         b += DTYPE_BYTES[param_dtype]
     return b

@@ -139,3 +139,18 @@ def test_hparam_structs_carry_the_clip_pointer():
     assert ctypes.sizeof(M.MuonGradBuffer) == 24
     h = M._hp(M.MuonHParamsC(0.02, 0.1, 0.95, 1, 1.5, -0.5, 0.0, 5, 1e-7, 0, 0.2))
     assert h.clip is None
+
+
+def test_adamw_step_ex_validates_state_dtypes():
+    L = M.lib()
+    P = ctypes.c_void_p
+    fake = P(4096)
+    hp = M.AdamWHParamsC(0.01, 0.9, 0.95, 1e-8, 0.1)
+    args = lambda mdt, vdt: (fake, 0, None, fake, 0, fake, mdt, fake, vdt, 8,  # noqa: E731
+                             ctypes.byref(hp), 1, None)
+    assert L.adamw_step_ex(*args(2, 0)) == M.MUON_ERR_BAD_DTYPE   # m cannot be fp16
+    assert L.adamw_step_ex(*args(0, 3)) == M.MUON_ERR_BAD_DTYPE
+    assert L.adamw_step_ex(*args(-1, 0)) == M.MUON_ERR_BAD_DTYPE
+    h0 = M.AdamWHParamsC(0.01, 0.9, 0.95, 1e-8, 0.1)
+    assert L.adamw_step_ex(fake, 0, None, fake, 0, fake, 1, fake, 2, 0, ctypes.byref(h0), 0,
+                           None) == M.MUON_ERR_INVALID_ARG  # step 0
