@@ -287,6 +287,58 @@ def main():
         del m_s, v_s, p_s, mst_s
     adamw_states = {"group": grp.name, "params": grp.numel, **states}
 
+    # ---- MuonClip (K2 answer section 4) on every W_q and W_k of the stack
+    # (the first two square matrices of each layer of 7), outside the step
+    muon_clip = None
+    sq = [m for m in wl.mats() if m[1] == m[2]]
+    if wl.name == "dense_d2048_l16":
+        qk = [sq[4 * l + j] for l in range(len(sq) // 4) for j in (0, 1)]
+        n_qk = sum(r * c for _, r, c in qk)
+        wclip = inp.params.clone()
+        fplan = M.muon_clip_plan_create([(o, r, c) for o, r, c in qk], wclip.numel(),
+                                        wl.param_dtype)
+        fws = fplan.alloc_workspace(dev)
+        d_head = 128
+        heads = [(o + h * d_head * c, d_head, c, c, (i // 2) * (r // d_head) + h)
+                 for i, (o, r, c) in enumerate(qk) for h in range(r // d_head)]
+        n_groups = len(heads) // 2
+        hplan = M.muon_clip_plan_create(heads, wclip.numel(), wl.param_dtype, n_groups)
+        norms0 = torch.empty(len(qk), device=dev)
+        M.muon_clip(fplan, wclip, "frobenius", 1e30, workspace=fws, norms_out=norms0)
+        torch.cuda.synchronize()
+        tau0 = 0.5 * float(norms0.min())
+
+        def time_seq(fns):
+            fns[0]()
+            a, b_ = ev(), ev()
+            a.record(stream)
+            for f in fns[1:]:
+                f()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b_) / (len(fns) - 1)
+
+        # each call clips every block (gamma ~ 0.9 against the previous call)
+        clipped = time_seq([lambda t=tau0 * 0.9 ** k: M.muon_clip(fplan, wclip, "frobenius", t,
+                                                                  workspace=fws)
+                            for k in range(6)])
+        unclipped = time_launch(lambda: M.muon_clip(fplan, wclip, "frobenius", 1e30,
+                                                    workspace=fws))
+        logits = torch.full((n_groups,), 400.0, device=dev)   # tau 100: gamma 1/2 everywhere
+        per_head = time_launch(lambda: M.muon_clip(hplan, wclip, "max_logit", 100.0,
+                                                   max_logits=logits))
+        eb = 2 if wl.param_dtype == "bf16" else 4
+
+        def entry(ms_, per_param):
+            nb = n_qk * per_param * eb
+            return {"ms": ms_, "bytes": nb, "gbps": nb / (ms_ * 1e-3) / 1e9}
+
+        muon_clip = {"params": n_qk, "blocks_frobenius": len(qk), "blocks_per_head": len(heads),
+                     "frobenius_all_clipped": entry(clipped, 3),
+                     "frobenius_none_clipped": entry(unclipped, 1),
+                     "max_logit_per_head_all_clipped": entry(per_head, 2)}
+        del wclip, fplan, hplan
+
     ceiling = mfma_ceiling()
 
     # ---- algorithmic work
@@ -376,6 +428,9 @@ def main():
         "guard": guard,
         # AdamW over the largest group with fp32 / 16-bit states, timed apart
         "adamw_state_dtypes": adamw_states,
+        # MuonClip over the stack's W_q / W_k, timed apart (bytes: read once
+        # for the norm, read + write when a block is rescaled)
+        "muon_clip": muon_clip,
     }
     if not args.no_cpu_baseline:
         # first layer of the stack: 4 square + 3 rectangular matrices

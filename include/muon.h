@@ -14,6 +14,10 @@
  *         norm is bounded by the Frobenius norm.
  *   [EP]  aihot.vn news item on MoonEP, "memory contract": expert weights
  *         live in one contiguous [E, H, H'] tensor addressed by row offset.
+ *   [K2]  section 4, MuonClip: the max attention logit grows in large Muon
+ *         runs; since ||x W||_2 <= ||x||_2 ||W||_2 <= ||x||_2 ||W||_F, a
+ *         clip of the weight's Frobenius norm bounds it; the method's author
+ *         acts on the max logit itself.
  *   [OPT] 5.4 (optimizer numerical faults under mixed precision): keep
  *         gradient clipping (clip_grad_norm) as a safety net, guard the
  *         step against Inf/NaN by skipping it, and watch statistics of the
@@ -283,6 +287,58 @@ size_t state_stats_workspace_size(void);
  * state_stats_workspace_size() bytes, 8-byte aligned. */
 int state_stats(const float* x, int64_t n, void* workspace, size_t workspace_bytes,
                 muon_state_stats_t* out, hipStream_t stream);
+
+/* ---- MuonClip ([K2] 4) ---------------------------------------------- */
+
+/* One block of the flat parameter buffer to clip: rows x cols elements,
+ * element (r, c) at offset + r * ld + c (ld >= cols).  A whole row-major
+ * [out, in] matrix has ld = cols; one attention head's block of rows of
+ * W_q or W_k is a block of that matrix's rows.  group: which entry of
+ * max_logits the block follows in max-logit mode (a head, or a layer). */
+typedef struct {
+  int64_t offset;
+  int64_t ld;
+  int32_t rows;
+  int32_t cols;
+  int32_t group;
+  int32_t reserved;
+} muon_clip_target_t;
+
+#define MUON_CLIP_FROBENIUS 0 /* gamma = min(1, tau / ||W||_F) per block */
+#define MUON_CLIP_MAX_LOGIT 1 /* gamma = sqrt(tau / S_group) when S_group > tau */
+
+typedef struct muon_clip_plan muon_clip_plan_t;
+
+/* Validates the blocks (inside [0, flat_numel), rows and cols >= 1,
+ * rows * cols < 2^31, no element in two blocks, group in [0, max(n_groups,
+ * 1))), splits them into fixed chunks and uploads the tables to the
+ * current device (the only device memory the library allocates; freed by
+ * muon_clip_plan_destroy).  *workspace_bytes: device workspace muon_clip
+ * needs in Frobenius mode (0 in max-logit mode).  targets is a host array. */
+int muon_clip_plan_create(const muon_clip_target_t* targets, int32_t n_targets,
+                          int64_t flat_numel, int32_t param_dtype, int32_t n_groups,
+                          muon_clip_plan_t** out, size_t* workspace_bytes);
+void muon_clip_plan_destroy(muon_clip_plan_t* plan);
+
+/* MuonClip on params (device, the plan's dtype, bf16 or fp32), in place,
+ * after the optimizer step ([K2] 4):
+ *   MUON_CLIP_FROBENIUS: per block, norm = ||W||_F (fp64 sum of squares in a
+ *     fixed order), gamma = tau / norm when norm > tau, else 1; then
+ *     ||W||_2 <= ||W||_F <= tau.
+ *   MUON_CLIP_MAX_LOGIT: per block, S = max_logits[group] (device, n_groups
+ *     floats: the largest attention logit of the forward pass), gamma =
+ *     sqrt(tau / S) when S > tau, else 1; scaling a head's W_q and W_k rows
+ *     by gamma scales its logits by gamma^2, so the largest becomes tau.
+ * A non-finite norm or S leaves the block unchanged (gamma = 1).  Blocks
+ * with gamma = 1 are not written.  New values: gamma * w in fp64, rounded
+ * to fp32 and then to the storage type (round to nearest even).
+ * tau: finite, > 0.  workspace: device, >= the plan's workspace_bytes,
+ * 8-byte aligned (Frobenius mode; may be null in max-logit mode).
+ * norms_out, scales_out: nullable device arrays of n_targets floats, the
+ * block's Frobenius norm before the clip (0 in max-logit mode) and gamma. */
+int muon_clip(const muon_clip_plan_t* plan, void* params, int32_t mode, float tau,
+              const float* max_logits, void* workspace, size_t workspace_bytes,
+              float* norms_out, float* scales_out, hipStream_t stream);
 
 const char* muon_status_string(int32_t status);
 const char* muon_last_error(void);

@@ -37,7 +37,11 @@ EXPORTED = [
     "muon_status_string",
     "muon_last_error", "grad_norm_clip_workspace_size", "grad_norm_clip",
     "state_stats_workspace_size", "state_stats",
+    "muon_clip_plan_create", "muon_clip_plan_destroy", "muon_clip",
 ]
+
+MUON_CLIP_FROBENIUS = 0
+MUON_CLIP_MAX_LOGIT = 1
 
 
 class MuonError(RuntimeError):
@@ -81,6 +85,11 @@ class MuonStateStats(ctypes.Structure):
     _fields_ = [("mean", ctypes.c_double), ("var", ctypes.c_double), ("min", ctypes.c_double),
                 ("max", ctypes.c_double), ("absmax", ctypes.c_double),
                 ("count", ctypes.c_int64), ("nonfinite", ctypes.c_int64)]
+
+
+class MuonClipTarget(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("ld", ctypes.c_int64), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class MuonPlanInfo(ctypes.Structure):
@@ -128,12 +137,18 @@ def lib() -> ctypes.CDLL:
     L.state_stats_workspace_size.argtypes = []
     L.state_stats_workspace_size.restype = SZ
     L.state_stats.argtypes = [P, I64, P, SZ, P, P]
+    L.muon_clip_plan_create.argtypes = [ctypes.POINTER(MuonClipTarget), I32, I64, I32, I32,
+                                        ctypes.POINTER(P), ctypes.POINTER(SZ)]
+    L.muon_clip_plan_destroy.argtypes = [P]
+    L.muon_clip_plan_destroy.restype = None
+    L.muon_clip.argtypes = [P, P, I32, ctypes.c_float, P, P, SZ, P, P, P]
     L.muon_status_string.argtypes = [I32]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_last_error.argtypes = []
     L.muon_last_error.restype = ctypes.c_char_p
     for name in EXPORTED:
-        if name not in ("muon_plan_destroy", "muon_status_string", "muon_last_error",
+        if name not in ("muon_plan_destroy", "muon_clip_plan_destroy", "muon_status_string",
+                        "muon_last_error",
                         "grad_norm_clip_workspace_size", "state_stats_workspace_size"):
             getattr(L, name).restype = ctypes.c_int
     _lib_handle = L
@@ -391,3 +406,73 @@ def read_state_stats(out) -> dict:
     """Copy device statistics to the host (synchronises)."""
     s = MuonStateStats.from_buffer_copy(bytes(out.cpu().numpy().tobytes()))
     return {k: getattr(s, k) for k, _ in MuonStateStats._fields_}
+
+
+# ---------------------------------------------------------------- MuonClip
+
+class MuonClipPlan:
+    """Owns a muon_clip_plan_t (destroyed with the object)."""
+
+    def __init__(self, handle: int, workspace_bytes: int, n_targets: int, n_groups: int,
+                 flat_numel: int, param_dtype: int):
+        self.handle = handle
+        self.workspace_bytes = workspace_bytes
+        self.n_targets = n_targets
+        self.n_groups = n_groups
+        self.flat_numel = flat_numel
+        self.param_dtype = param_dtype
+
+    def alloc_workspace(self, device="cuda"):
+        import torch
+        return torch.empty(max(8, self.workspace_bytes), dtype=torch.uint8, device=device)
+
+    def close(self):
+        if self.handle:
+            lib().muon_clip_plan_destroy(ctypes.c_void_p(self.handle))
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def muon_clip_plan_create(targets, flat_numel: int, param_dtype, n_groups: int = 0
+                          ) -> MuonClipPlan:
+    """targets: (offset, rows, cols[, ld[, group]]) per block (ld defaults
+    to cols, group to 0)."""
+    arr = (MuonClipTarget * max(1, len(targets)))()
+    for i, t in enumerate(targets):
+        off, rows, cols = int(t[0]), int(t[1]), int(t[2])
+        ld = int(t[3]) if len(t) > 3 else cols
+        group = int(t[4]) if len(t) > 4 else 0
+        arr[i] = MuonClipTarget(off, ld, rows, cols, group, 0)
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+    pd = dtype_code(param_dtype)
+    _check(lib().muon_clip_plan_create(arr, len(targets), int(flat_numel), pd, int(n_groups),
+                                       ctypes.byref(h), ctypes.byref(ws)))
+    return MuonClipPlan(h.value, ws.value, len(targets), int(n_groups), int(flat_numel), pd)
+
+
+def muon_clip(plan: MuonClipPlan, params, mode, tau: float, max_logits=None, workspace=None,
+              norms_out=None, scales_out=None, stream=None) -> None:
+    """MuonClip in place on ``params`` (the flat buffer the plan describes).
+    mode: "frobenius" / MUON_CLIP_FROBENIUS or "max_logit" / MUON_CLIP_MAX_LOGIT."""
+    import torch
+    m = {"frobenius": MUON_CLIP_FROBENIUS, "max_logit": MUON_CLIP_MAX_LOGIT}.get(mode, mode)
+    if params.numel() < plan.flat_numel or dtype_code(params.dtype) != plan.param_dtype:
+        raise MuonError(MUON_ERR_INVALID_ARG, "params do not match the clip plan")
+    if m == MUON_CLIP_MAX_LOGIT and (max_logits is None or max_logits.dtype != torch.float32
+                                     or max_logits.numel() < plan.n_groups):
+        raise MuonError(MUON_ERR_INVALID_ARG, "max_logits: n_groups fp32 values")
+    for o in (norms_out, scales_out):
+        if o is not None and (o.dtype != torch.float32 or o.numel() < plan.n_targets):
+            raise MuonError(MUON_ERR_INVALID_ARG, "norms_out / scales_out: n_targets fp32")
+    if workspace is None and m == MUON_CLIP_FROBENIUS:
+        workspace = plan.alloc_workspace(params.device)
+    _check(lib().muon_clip(ctypes.c_void_p(plan.handle), _ptr(params), int(m), float(tau),
+                           _ptr(max_logits), _ptr(workspace),
+                           workspace.numel() if workspace is not None else 0,
+                           _ptr(norms_out), _ptr(scales_out), _stream(stream)))

@@ -45,6 +45,9 @@ struct Wave {
 
 }  // namespace
 
+int muon::set_error(int code, const std::string& msg) { return fail(code, msg); }
+int muon::set_hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+
 struct muon_plan {
   int device = 0;
   int n_cu = 256;  // compute units of the plan's device (persistent grid size)

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace muon {
 
 // Edge of the elementwise tiles used by the momentum and apply kernels.
@@ -97,6 +99,11 @@ hipError_t launch_clip_finalize(const double* partials, int n_parts, float max_n
 constexpr int kStatsPartialBytes = 64;
 hipError_t launch_state_stats(const float* x, int64_t n, void* partials, void* out,
                               hipStream_t s);
+
+// Error reporting shared by the host sources: record the message for
+// muon_last_error() on the calling thread and return the status code.
+int set_error(int code, const std::string& msg);
+int set_hip_error(hipError_t e, const char* what);
 
 // bf16 <-> fp32 (bf16 stored as its 16-bit pattern)
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

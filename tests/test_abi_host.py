@@ -154,3 +154,42 @@ def test_adamw_step_ex_validates_state_dtypes():
     h0 = M.AdamWHParamsC(0.01, 0.9, 0.95, 1e-8, 0.1)
     assert L.adamw_step_ex(fake, 0, None, fake, 0, fake, 1, fake, 2, 0, ctypes.byref(h0), 0,
                            None) == M.MUON_ERR_INVALID_ARG  # step 0
+
+
+def _clip_plan_rc(targets, flat_numel=1000, dtype=1, n_groups=0):
+    L = M.lib()
+    arr = (M.MuonClipTarget * max(1, len(targets)))(*[M.MuonClipTarget(*t) for t in targets])
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+    return L.muon_clip_plan_create(arr, len(targets), flat_numel, dtype, n_groups,
+                                   ctypes.byref(h), ctypes.byref(ws))
+
+
+def test_clip_plan_validates_before_any_hip_call():
+    # (offset, ld, rows, cols, group, reserved)
+    assert ctypes.sizeof(M.MuonClipTarget) == 32
+    assert _clip_plan_rc([(0, 10, 10, 10, 0, 0)], dtype=2) == M.MUON_ERR_BAD_DTYPE
+    assert _clip_plan_rc([(0, 10, 0, 10, 0, 0)]) == M.MUON_ERR_BAD_SHAPE          # rows 0
+    assert _clip_plan_rc([(0, 5, 2, 10, 0, 0)]) == M.MUON_ERR_BAD_SHAPE           # ld < cols
+    assert _clip_plan_rc([(-1, 10, 2, 10, 0, 0)]) == M.MUON_ERR_BAD_SHAPE         # offset < 0
+    assert _clip_plan_rc([(991, 10, 1, 10, 0, 0)]) == M.MUON_ERR_BAD_SHAPE        # past the end
+    assert _clip_plan_rc([(0, 100, 10, 10, 0, 0)], flat_numel=909) == M.MUON_ERR_BAD_SHAPE
+    assert _clip_plan_rc([(0, 100, 10, 10, 0, 0)], flat_numel=910) != M.MUON_ERR_BAD_SHAPE
+    assert _clip_plan_rc([(0, 1 << 16, 1 << 16, 1 << 16, 0, 0)],
+                         flat_numel=1 << 40) == M.MUON_ERR_BAD_SHAPE             # > 2^31 elements
+    assert _clip_plan_rc([(0, 10, 1, 10, 1, 0)], n_groups=1) == M.MUON_ERR_INVALID_ARG
+    assert _clip_plan_rc([(0, 10, 1, 10, -1, 0)]) == M.MUON_ERR_INVALID_ARG
+    # overlaps: contiguous blocks, and interleaved strided blocks
+    assert _clip_plan_rc([(0, 10, 2, 10, 0, 0), (19, 10, 1, 10, 0, 0)]) == M.MUON_ERR_OVERLAP
+    assert _clip_plan_rc([(0, 20, 5, 10, 0, 0), (9, 20, 5, 10, 0, 0)]) == M.MUON_ERR_OVERLAP
+    # two column blocks of one matrix interleave without sharing elements:
+    # validation passes and the call gets as far as the device (no GPU here)
+    rc = _clip_plan_rc([(0, 20, 5, 10, 0, 0), (10, 20, 5, 10, 0, 0)])
+    assert rc not in (M.MUON_ERR_OVERLAP, M.MUON_ERR_BAD_SHAPE, M.MUON_ERR_INVALID_ARG)
+    L = M.lib()
+    assert L.muon_clip_plan_create(None, 1, 10, 1, 0, ctypes.byref(ctypes.c_void_p()),
+                                   None) == M.MUON_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(4096)
+    assert L.muon_clip(None, fake, 0, 1.0, None, fake, 8, None, None, None) == \
+        M.MUON_ERR_INVALID_ARG
+    L.muon_clip_plan_destroy(None)  # a null plan is a no-op
