@@ -294,7 +294,10 @@ def main():
     if wl.name == "dense_d2048_l16":
         qk = [sq[4 * l + j] for l in range(len(sq) // 4) for j in (0, 1)]
         n_qk = sum(r * c for _, r, c in qk)
-        wclip = inp.params.clone()
+        # in place on the step's parameters: the timed region is over and
+        # nothing reads them afterwards (a clone would be the largest device
+        # copy of the run, which the traffic calibration must not meet)
+        wclip = inp.params
         fplan = M.muon_clip_plan_create([(o, r, c) for o, r, c in qk], wclip.numel(),
                                         wl.param_dtype)
         fws = fplan.alloc_workspace(dev)
@@ -337,7 +340,7 @@ def main():
                      "frobenius_all_clipped": entry(clipped, 3),
                      "frobenius_none_clipped": entry(unclipped, 1),
                      "max_logit_per_head_all_clipped": entry(per_head, 2)}
-        del wclip, fplan, hplan
+        del fplan, hplan
 
     ceiling = mfma_ceiling()
 
