@@ -70,7 +70,22 @@ def test_strided_blocks_touch_only_their_elements():
         touched[idx] = True
         assert np.linalg.norm(out[idx]) == pytest.approx(1.0, rel=1e-14)
     assert np.array_equal(out[~touched], flat[~touched])
-    assert touched.sum() == 20
+    # the blocks' flat indices, written out by hand: rows 0-1 and 4-5 of a
+    # matrix starting at 3 with 7 elements per row, first 5 columns
+    want = [3, 4, 5, 6, 7, 10, 11, 12, 13, 14, 31, 32, 33, 34, 35, 38, 39, 40, 41, 42]
+    assert np.flatnonzero(touched).tolist() == want
+
+
+def test_attention_max_logit_by_hand():
+    # x = I2, W_q = [1, 2], W_k = [3, -1]: q = (1, 2), k = (3, -1), logits
+    # q_i k_j = [[3, -1], [6, -2]]: the largest is 6
+    x = np.eye(2)
+    assert C.attention_max_logit(x, np.array([[1.0, 2.0]]), np.array([[3.0, -1.0]])) == 6.0
+    # W_q = I, W_k swaps the two features: q = x = [[1, 1], [2, -1]],
+    # k = [[1, 1], [-1, 2]], logits [[2, 1], [1, -4]]: the largest is 2
+    # (with k taken from W_q it would be 5)
+    x = np.array([[1.0, 1.0], [2.0, -1.0]])
+    assert C.attention_max_logit(x, np.eye(2), np.array([[0.0, 1.0], [1.0, 0.0]])) == 2.0
 
 
 def _heads(rng, n_heads, d_head, d_model, scale):

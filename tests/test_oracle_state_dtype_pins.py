@@ -32,6 +32,19 @@ def test_fp16_rounding_fixed_points():
     assert O.round_to([1 + 2 ** -11], "fp16")[0] == 1.0
 
 
+def test_fp16_rounds_the_fp32_value():
+    # The stored state is the fp16 rounding of the fp32 value the step
+    # computes, not of the exact one.  1 + 2^-11 + 2^-30 is above the
+    # midpoint between 1 and 1 + 2^-10, so it would round up directly; in
+    # fp32 (23 fraction bits) it is the midpoint itself, which ties to 1.
+    x = 1 + 2 ** -11 + 2 ** -30
+    assert float(np.float16(x)) == 1 + 2 ** -10      # direct rounding, for contrast
+    assert O.fp16_round([x])[0] == 1.0
+    # the same for bf16 (8 significant bits): 1 + 2^-8 is the midpoint
+    y = 1 + 2 ** -8 + 2 ** -30
+    assert O.bf16_round([y])[0] == 1.0
+
+
 def test_first_step_states_in_16_bit():
     # t = 1 from zero: m1 = (1 - b1) g, v1 = (1 - b2) g^2, stored rounded
     hp = O.AdamWHP(lr=0.01, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0)
