@@ -271,21 +271,23 @@ def main():
 
     # ---- AdamW with compressed optimizer states (optimizer tutorial 2.4 /
     # 3.3: 16-bit m and v), on the largest AdamW group, fresh zero states
-    big = max(range(len(adam)), key=lambda gi: wl.adam[gi].numel)
-    ga, grp = adam[big], wl.adam[big]
-    states = {}
-    for mdt, vdt in (("fp32", "fp32"), ("bf16", "bf16"), ("bf16", "fp16")):
-        tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
-        m_s = torch.zeros(grp.numel, dtype=tdt[mdt], device=dev)
-        v_s = torch.zeros(grp.numel, dtype=tdt[vdt], device=dev)
-        p_s, mst_s = ga.param.clone(), (ga.master.clone() if ga.master is not None else None)
-        ms_ = time_launch(lambda: M.adamw_step(p_s, mst_s, ga.grad, m_s, v_s, ahp, 1))
-        nb = grp.numel * W.adamw_bytes_per_param(grp.param_dtype, grp.grad_dtype, grp.master,
-                                                 mdt, vdt)
-        states[f"m_{mdt}_v_{vdt}"] = {"ms": ms_, "bytes": nb, "gbps": nb / (ms_ * 1e-3) / 1e9,
-                                      "bytes_per_param": nb // grp.numel}
-        del m_s, v_s, p_s, mst_s
-    adamw_states = {"group": grp.name, "params": grp.numel, **states}
+    adamw_states = None
+    if adam:
+        big = max(range(len(adam)), key=lambda gi: wl.adam[gi].numel)
+        ga, grp = adam[big], wl.adam[big]
+        states = {}
+        for mdt, vdt in (("fp32", "fp32"), ("bf16", "bf16"), ("bf16", "fp16")):
+            tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
+            m_s = torch.zeros(grp.numel, dtype=tdt[mdt], device=dev)
+            v_s = torch.zeros(grp.numel, dtype=tdt[vdt], device=dev)
+            p_s, mst_s = ga.param.clone(), (ga.master.clone() if ga.master is not None else None)
+            ms_ = time_launch(lambda: M.adamw_step(p_s, mst_s, ga.grad, m_s, v_s, ahp, 1))
+            nb = grp.numel * W.adamw_bytes_per_param(grp.param_dtype, grp.grad_dtype, grp.master,
+                                                     mdt, vdt)
+            states[f"m_{mdt}_v_{vdt}"] = {"ms": ms_, "bytes": nb, "gbps": nb / (ms_ * 1e-3) / 1e9,
+                                          "bytes_per_param": nb // grp.numel}
+            del m_s, v_s, p_s, mst_s
+        adamw_states = {"group": grp.name, "params": grp.numel, **states}
 
     # ---- MuonClip (K2 answer section 4) on every W_q and W_k of the stack
     # (the first two square matrices of each layer of 7), outside the step
