@@ -194,6 +194,30 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _buf(t, name: str, min_numel: int = 0, dtypes=None, optional: bool = False):
+    """Checks a tensor before its address crosses the C ABI, which cannot
+    see sizes: a GPU tensor, contiguous, with at least ``min_numel``
+    elements of an allowed dtype.  Returns it."""
+    if t is None:
+        if optional:
+            return None
+        raise MuonError(MUON_ERR_INVALID_ARG, f"{name} is None")
+    if not getattr(t, "is_cuda", False):
+        raise MuonError(MUON_ERR_INVALID_ARG, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise MuonError(MUON_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if t.numel() < min_numel:
+        raise MuonError(MUON_ERR_INVALID_ARG,
+                        f"{name} has {t.numel()} elements, needs at least {min_numel}")
+    if dtypes is not None and dtype_code(t.dtype) not in dtypes:
+        raise MuonError(MUON_ERR_BAD_DTYPE, f"{name} has dtype {t.dtype}")
+    return t
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -232,10 +256,14 @@ def _ahp(hp, clip=None) -> AdamWHParamsC:
 class MuonPlan:
     """Owns a muon_plan_t (destroyed with the object)."""
 
-    def __init__(self, handle: int, workspace_bytes: int, n_mats: int):
+    def __init__(self, handle: int, workspace_bytes: int, n_mats: int, flat_numel: int = 0,
+                 param_dtype: int = MUON_DTYPE_BF16, grad_dtype: int = MUON_DTYPE_BF16):
         self.handle = handle
         self.workspace_bytes = workspace_bytes
         self.n_mats = n_mats
+        self.flat_numel = flat_numel
+        self.param_dtype = param_dtype
+        self.grad_dtype = grad_dtype
 
     def info(self) -> MuonPlanInfo:
         return muon_plan_get_info(self)
@@ -274,7 +302,8 @@ def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="b
     _check(lib().muon_plan_create(arr, len(mats), int(flat_numel), dtype_code(param_dtype),
                                   dtype_code(grad_dtype), dtype_code(ns_dtype),
                                   int(workspace_cap), ctypes.byref(h), ctypes.byref(ws)))
-    return MuonPlan(h.value, ws.value, len(mats))
+    return MuonPlan(h.value, ws.value, len(mats), int(flat_numel), dtype_code(param_dtype),
+                    dtype_code(grad_dtype))
 
 
 def muon_plan_destroy(plan: MuonPlan) -> None:
@@ -287,48 +316,76 @@ def muon_plan_get_info(plan: MuonPlan) -> MuonPlanInfo:
     return info
 
 
+F32 = (MUON_DTYPE_FP32,)
+
+
+def _flat_args(plan: MuonPlan, params=None, grads=None, momentum=None, out_update=None):
+    n = plan.flat_numel
+    if params is not None:
+        _buf(params, "params", n, (plan.param_dtype,))
+    if grads is not None:
+        _buf(grads, "grads", n, (plan.grad_dtype,))
+    if momentum is not None:
+        _buf(momentum, "momentum", n, F32)
+    _buf(out_update, "out_update", n, F32, optional=True)
+
+
 def muon_step(plan: MuonPlan, params, grads, momentum, workspace, hp, out_update=None,
               stream=None, clip=None) -> None:
     """clip: optional device clip state from grad_norm_clip (scale and guard)."""
+    _flat_args(plan, _buf(params, "params"), _buf(grads, "grads"), _buf(momentum, "momentum"),
+               out_update)
+    _buf(workspace, "workspace")
     h = _hp(hp, clip)
     _check(lib().muon_step(ctypes.c_void_p(plan.handle), _ptr(params), _ptr(grads),
-                           _ptr(momentum), _ptr(workspace), workspace.numel(), ctypes.byref(h),
+                           _ptr(momentum), _ptr(workspace), _nbytes(workspace), ctypes.byref(h),
                            _ptr(out_update), _stream(stream)))
 
 
 def muon_stage_momentum(plan: MuonPlan, wave: int, grads, momentum, workspace, hp,
                         stream=None, clip=None) -> None:
+    _flat_args(plan, grads=_buf(grads, "grads"), momentum=_buf(momentum, "momentum"))
+    _buf(workspace, "workspace")
     h = _hp(hp, clip)
     _check(lib().muon_stage_momentum(ctypes.c_void_p(plan.handle), wave, _ptr(grads),
-                                     _ptr(momentum), _ptr(workspace), workspace.numel(),
+                                     _ptr(momentum), _ptr(workspace), _nbytes(workspace),
                                      ctypes.byref(h), _stream(stream)))
 
 
 def muon_stage_ns_phase(plan: MuonPlan, wave: int, workspace, hp, iter: int, phase: int,
                         stream=None) -> None:
+    _buf(workspace, "workspace")
     h = _hp(hp)
     _check(lib().muon_stage_ns_phase(ctypes.c_void_p(plan.handle), wave, _ptr(workspace),
-                                     workspace.numel(), ctypes.byref(h), iter, phase,
+                                     _nbytes(workspace), ctypes.byref(h), iter, phase,
                                      _stream(stream)))
 
 
 def muon_stage_apply(plan: MuonPlan, wave: int, params, workspace, hp, out_update=None,
                      stream=None, clip=None) -> None:
+    _flat_args(plan, params=_buf(params, "params"), out_update=out_update)
+    _buf(workspace, "workspace")
     h = _hp(hp, clip)
     _check(lib().muon_stage_apply(ctypes.c_void_p(plan.handle), wave, _ptr(params),
-                                  _ptr(workspace), workspace.numel(), ctypes.byref(h),
+                                  _ptr(workspace), _nbytes(workspace), ctypes.byref(h),
                                   _ptr(out_update), _stream(stream)))
 
 
 def muon_stage_export_x(plan: MuonPlan, wave: int, workspace, iter_done: int, out,
                         stream=None) -> None:
+    """out: fp32, flat_numel elements (the wave's matrices at their offsets)."""
+    _buf(workspace, "workspace")
+    _buf(out, "out", plan.flat_numel, F32)
     _check(lib().muon_stage_export_x(ctypes.c_void_p(plan.handle), wave, _ptr(workspace),
-                                     workspace.numel(), iter_done, _ptr(out), _stream(stream)))
+                                     _nbytes(workspace), iter_done, _ptr(out), _stream(stream)))
 
 
 def muon_stage_export_norms(plan: MuonPlan, wave: int, workspace, out, stream=None) -> None:
+    """out: fp32, at least as many elements as the wave has matrices."""
+    _buf(workspace, "workspace")
+    _buf(out, "out", 1 if plan.n_mats else 0, F32)
     _check(lib().muon_stage_export_norms(ctypes.c_void_p(plan.handle), wave, _ptr(workspace),
-                                         workspace.numel(), _ptr(out), _stream(stream)))
+                                         _nbytes(workspace), _ptr(out), _stream(stream)))
 
 
 def adamw_step(params, master, grads, exp_avg, exp_avg_sq, hp, step: int, stream=None,
@@ -337,9 +394,10 @@ def adamw_step(params, master, grads, exp_avg, exp_avg_sq, hp, step: int, stream
     exp_avg may be fp32 or bf16 and exp_avg_sq fp32, bf16 or fp16 (the
     compressed states of adamw_step_ex); clip: optional device clip state
     from grad_norm_clip."""
-    n = params.numel()
+    n = _buf(params, "params").numel()
     for name, t in (("grads", grads), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq),
                     ("master", master)):
+        _buf(t, name, optional=name == "master")
         if t is not None and t.numel() != n:
             raise MuonError(MUON_ERR_INVALID_ARG, f"{name} has {t.numel()} elements, expected {n}")
     h = _ahp(hp, clip)
@@ -364,16 +422,22 @@ def grad_norm_clip(grads: Sequence, max_norm: float, eps: float = 1e-6, out=None
     bufs = (MuonGradBuffer * max(1, len(grads)))()
     dev = None
     for k, g in enumerate(grads):
-        bufs[k] = MuonGradBuffer(_ptr(g), int(g.numel()), dtype_code(g.dtype), 0)
+        _buf(g, f"grads[{k}]")
         dev = g.device
     dev = dev if dev is not None else torch.device("cuda")
     if out is None:
         out = torch.zeros(16, dtype=torch.uint8, device=dev)
+    if _nbytes(_buf(out, "out")) < ctypes.sizeof(MuonClipState):
+        raise MuonError(MUON_ERR_INVALID_ARG, "out: 16 bytes of device memory")
     need = grad_norm_clip_workspace_size(len(grads))
     if workspace is None:
         workspace = torch.empty(max(8, need), dtype=torch.uint8, device=dev)
-    _check(lib().grad_norm_clip(bufs, len(grads), float(max_norm), float(eps), _ptr(workspace),
-                                workspace.numel(), _ptr(out), _stream(stream)))
+    _buf(workspace, "workspace")
+    for k, g in enumerate(grads):
+        bufs[k] = MuonGradBuffer(_ptr(g), int(g.numel()), dtype_code(g.dtype), 0)
+    _check(lib().grad_norm_clip(bufs, len(grads), float(max_norm), float(eps),
+                                _ptr(workspace), _nbytes(workspace), _ptr(out),
+                                _stream(stream)))
     return out
 
 
@@ -391,14 +455,15 @@ def state_stats(x, out=None, workspace=None, stream=None):
     """Statistics of a fp32 state tensor into ``out`` (a 56-byte device
     tensor, allocated if None), returned."""
     import torch
-    if x.dtype != torch.float32:
-        raise MuonError(MUON_ERR_BAD_DTYPE, "state_stats takes fp32 buffers")
+    _buf(x, "x", dtypes=F32)
     if out is None:
         out = torch.zeros(ctypes.sizeof(MuonStateStats), dtype=torch.uint8, device=x.device)
+    if _nbytes(_buf(out, "out")) < ctypes.sizeof(MuonStateStats):
+        raise MuonError(MUON_ERR_INVALID_ARG, "out: 56 bytes of device memory")
     if workspace is None:
         workspace = torch.empty(state_stats_workspace_size(), dtype=torch.uint8, device=x.device)
-    _check(lib().state_stats(_ptr(x), int(x.numel()), _ptr(workspace), workspace.numel(),
-                             _ptr(out), _stream(stream)))
+    _check(lib().state_stats(_ptr(x), int(x.numel()), _ptr(_buf(workspace, "workspace")),
+                             _nbytes(workspace), _ptr(out), _stream(stream)))
     return out
 
 
@@ -460,19 +525,16 @@ def muon_clip(plan: MuonClipPlan, params, mode, tau: float, max_logits=None, wor
               norms_out=None, scales_out=None, stream=None) -> None:
     """MuonClip in place on ``params`` (the flat buffer the plan describes).
     mode: "frobenius" / MUON_CLIP_FROBENIUS or "max_logit" / MUON_CLIP_MAX_LOGIT."""
-    import torch
     m = {"frobenius": MUON_CLIP_FROBENIUS, "max_logit": MUON_CLIP_MAX_LOGIT}.get(mode, mode)
-    if params.numel() < plan.flat_numel or dtype_code(params.dtype) != plan.param_dtype:
-        raise MuonError(MUON_ERR_INVALID_ARG, "params do not match the clip plan")
-    if m == MUON_CLIP_MAX_LOGIT and (max_logits is None or max_logits.dtype != torch.float32
-                                     or max_logits.numel() < plan.n_groups):
-        raise MuonError(MUON_ERR_INVALID_ARG, "max_logits: n_groups fp32 values")
-    for o in (norms_out, scales_out):
-        if o is not None and (o.dtype != torch.float32 or o.numel() < plan.n_targets):
-            raise MuonError(MUON_ERR_INVALID_ARG, "norms_out / scales_out: n_targets fp32")
+    _buf(params, "params", plan.flat_numel, (plan.param_dtype,))
+    if m == MUON_CLIP_MAX_LOGIT:
+        _buf(max_logits, "max_logits", plan.n_groups, F32)
+    _buf(norms_out, "norms_out", plan.n_targets, F32, optional=True)
+    _buf(scales_out, "scales_out", plan.n_targets, F32, optional=True)
     if workspace is None and m == MUON_CLIP_FROBENIUS:
         workspace = plan.alloc_workspace(params.device)
+    _buf(workspace, "workspace", optional=True)
     _check(lib().muon_clip(ctypes.c_void_p(plan.handle), _ptr(params), int(m), float(tau),
                            _ptr(max_logits), _ptr(workspace),
-                           workspace.numel() if workspace is not None else 0,
+                           _nbytes(workspace) if workspace is not None else 0,
                            _ptr(norms_out), _ptr(scales_out), _stream(stream)))
