@@ -145,6 +145,8 @@ typedef struct {
   int64_t bx_tiles;           /* B X tiles, all waves */
   size_t workspace_bytes;
   double ns_flops_per_iter_alg;   /* algorithmic flops per NS iteration with c != 0 */
+  int32_t small_mats;         /* matrices on the fused small-matrix path (below) */
+  int32_t reserved;
 } muon_plan_info_t;
 
 /* Host-only sizing: validates exactly as muon_plan_create and returns the
@@ -161,6 +163,18 @@ int muon_workspace_size(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_
 int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                      int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
                      size_t workspace_cap, muon_plan_t** out, size_t* workspace_bytes);
+
+/* muon_plan_create with flags.  By default (flags 0) a matrix with bf16 NS
+ * whose padded short side m_k (min(rows, cols) rounded up to 32) is at
+ * most 128 and whose m_k * n_k is at most 32768 runs each NS iteration in
+ * one workgroup with X, A and B in LDS (one launch per iteration instead of
+ * three single-tile launches); its iterates are bitwise those of the tiled
+ * path.  MUON_PLAN_TILED_ONLY puts every matrix on the tiled path. */
+#define MUON_PLAN_TILED_ONLY 1u
+int muon_plan_create_ex(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
+                        int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
+                        size_t workspace_cap, uint32_t flags, muon_plan_t** out,
+                        size_t* workspace_bytes);
 
 void muon_plan_destroy(muon_plan_t* plan);
 

@@ -31,7 +31,8 @@ MUON_DTYPE_BF16 = 1
 MUON_DTYPE_FP16 = 2
 
 EXPORTED = [
-    "muon_workspace_size", "muon_plan_create", "muon_plan_destroy", "muon_plan_get_info",
+    "muon_workspace_size", "muon_plan_create", "muon_plan_create_ex", "muon_plan_destroy",
+    "muon_plan_get_info",
     "muon_step", "muon_stage_momentum", "muon_stage_ns_phase", "muon_stage_apply",
     "muon_stage_export_x", "muon_stage_export_norms", "adamw_step", "adamw_step_ex",
     "muon_status_string",
@@ -97,7 +98,8 @@ class MuonPlanInfo(ctypes.Structure):
                 ("tile", ctypes.c_int32), ("ns_dtype", ctypes.c_int32),
                 ("k1_tiles", ctypes.c_int64), ("syrk_tiles", ctypes.c_int64),
                 ("bx_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-                ("ns_flops_per_iter_alg", ctypes.c_double)]
+                ("ns_flops_per_iter_alg", ctypes.c_double), ("small_mats", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib_handle = None
@@ -117,6 +119,8 @@ def lib() -> ctypes.CDLL:
     L.muon_workspace_size.argtypes = [mats_p, I32, I64, I32, I32, I32, SZ, ctypes.POINTER(SZ)]
     L.muon_plan_create.argtypes = [mats_p, I32, I64, I32, I32, I32, SZ, ctypes.POINTER(P),
                                    ctypes.POINTER(SZ)]
+    L.muon_plan_create_ex.argtypes = [mats_p, I32, I64, I32, I32, I32, SZ, ctypes.c_uint32,
+                                      ctypes.POINTER(P), ctypes.POINTER(SZ)]
     L.muon_plan_destroy.argtypes = [P]
     L.muon_plan_destroy.restype = None
     L.muon_plan_get_info.argtypes = [P, ctypes.POINTER(MuonPlanInfo)]
@@ -294,14 +298,21 @@ def muon_workspace_size(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype
     return out.value
 
 
+MUON_PLAN_TILED_ONLY = 1
+
+
 def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="bf16",
-                     workspace_cap: int = 0) -> MuonPlan:
+                     workspace_cap: int = 0, tiled_only: bool = False) -> MuonPlan:
+    """tiled_only: every matrix on the tiled NS path (no fused small-matrix
+    kernel); results are bitwise the same either way."""
     arr = _mats_array(mats)
     h = ctypes.c_void_p(0)
     ws = ctypes.c_size_t(0)
-    _check(lib().muon_plan_create(arr, len(mats), int(flat_numel), dtype_code(param_dtype),
-                                  dtype_code(grad_dtype), dtype_code(ns_dtype),
-                                  int(workspace_cap), ctypes.byref(h), ctypes.byref(ws)))
+    _check(lib().muon_plan_create_ex(arr, len(mats), int(flat_numel), dtype_code(param_dtype),
+                                     dtype_code(grad_dtype), dtype_code(ns_dtype),
+                                     int(workspace_cap),
+                                     MUON_PLAN_TILED_ONLY if tiled_only else 0,
+                                     ctypes.byref(h), ctypes.byref(ws)))
     return MuonPlan(h.value, ws.value, len(mats), int(flat_numel), dtype_code(param_dtype),
                     dtype_code(grad_dtype))
 

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmuon.so")
-SOURCES = ["muon_abi.hip", "elementwise.hip", "ns_gemm.hip", "guard.hip", "clip.hip"]
+SOURCES = ["muon_abi.hip", "elementwise.hip", "ns_gemm.hip", "ns_small.hip", "guard.hip", "clip.hip"]
 # stand-alone measurement program: the GPU's sustained bf16 MFMA rate
 CEILING = os.path.join(PKG, "mfma_ceiling")
 CEILING_SRC = "mfma_ceiling.hip"

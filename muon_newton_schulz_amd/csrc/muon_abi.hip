@@ -39,6 +39,7 @@ struct Wave {
   int64_t k1_begin = 0, k1_count = 0;      // into the k1 item table
   int64_t syrk_begin = 0, syrk_count = 0;  // phases 1 and 2 share the list
   int64_t bx_begin = 0, bx_count = 0;
+  int64_t small_begin = 0, small_count = 0;  // into the small-matrix table
   size_t partial_off = 0, norm_off = 0, inv_off = 0;  // byte offsets in the workspace
   size_t bytes = 0;
 };
@@ -58,6 +59,7 @@ struct muon_plan {
   size_t ws_bytes = 0;
   std::vector<MatDev> mats;
   std::vector<Item> k1_items, syrk_items, bx_items;
+  std::vector<int32_t> small_list;  // matrices run by the fused small-matrix kernel
   std::vector<Wave> waves;
   // device copies
   void* d_tables = nullptr;
@@ -65,6 +67,7 @@ struct muon_plan {
   Item* d_k1 = nullptr;
   Item* d_syrk = nullptr;
   Item* d_bx = nullptr;
+  int32_t* d_small = nullptr;
   double flops_per_iter = 0.0;
 };
 
@@ -120,7 +123,9 @@ void emit_super_tiles(int mat, int rows, int cols, bool tri, std::vector<Item>& 
 // Build every host-side table; no HIP call.
 int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype, size_t workspace_cap,
-               muon_plan& p) {
+               uint32_t flags, muon_plan& p) {
+  if ((flags & ~static_cast<uint32_t>(MUON_PLAN_TILED_ONLY)) != 0)
+    return fail(MUON_ERR_INVALID_ARG, "unknown plan flags");
   if (n_mats < 0) return fail(MUON_ERR_INVALID_ARG, "n_mats < 0");
   if (n_mats > 0 && mats == nullptr) return fail(MUON_ERR_INVALID_ARG, "mats is null");
   if (flat_numel < 0) return fail(MUON_ERR_INVALID_ARG, "flat_numel < 0");
@@ -177,6 +182,11 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     d.n_pad = static_cast<int32_t>(round_up(std::max(d.rows, d.cols), T));
     d.m_k = static_cast<int32_t>(round_up(std::min(d.rows, d.cols), muon::kNsKStep));
     d.n_k = static_cast<int32_t>(round_up(std::max(d.rows, d.cols), muon::kNsKStep));
+    d.small = (ns_dtype == MUON_DTYPE_BF16 && !(flags & MUON_PLAN_TILED_ONLY) &&
+               d.m_k <= muon::kSmallM &&
+               static_cast<int64_t>(d.m_k) * d.n_k <= muon::kSmallElems)
+                  ? 1
+                  : 0;
     const double m = std::min(d.rows, d.cols), n = std::max(d.rows, d.cols);
     p.flops_per_iter += m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n;
   }
@@ -260,7 +270,12 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     // tiles in super-tile order, then permuted so that every XCD receives
     // whole groups of neighbouring tiles (see xcd_dispatch_order).
     std::vector<int> order;
-    for (int m = w.mat_begin; m < w.mat_end; ++m) order.push_back(m);
+    w.small_begin = static_cast<int64_t>(p.small_list.size());
+    for (int m = w.mat_begin; m < w.mat_end; ++m) {
+      if (p.mats[m].small) p.small_list.push_back(m);
+      else order.push_back(m);
+    }
+    w.small_count = static_cast<int64_t>(p.small_list.size()) - w.small_begin;
     std::vector<Item> syrk_l, bx_l;
     std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
       return p.mats[x].n_pad > p.mats[y].n_pad;
@@ -296,7 +311,8 @@ int upload_plan(muon_plan& p) {
   const size_t b_k1 = align_up(p.k1_items.size() * sizeof(Item), kAlign);
   const size_t b_syrk = align_up(p.syrk_items.size() * sizeof(Item), kAlign);
   const size_t b_bx = align_up(p.bx_items.size() * sizeof(Item), kAlign);
-  const size_t total = b_mats + b_k1 + b_syrk + b_bx;
+  const size_t b_small = align_up(p.small_list.size() * sizeof(int32_t), kAlign);
+  const size_t total = b_mats + b_k1 + b_syrk + b_bx + b_small;
   if (total == 0) return MUON_OK;
   e = hipMalloc(&p.d_tables, total);
   if (e != hipSuccess) return hip_fail(e, "hipMalloc(plan tables)");
@@ -305,12 +321,15 @@ int upload_plan(muon_plan& p) {
   p.d_k1 = reinterpret_cast<Item*>(base + b_mats);
   p.d_syrk = reinterpret_cast<Item*>(base + b_mats + b_k1);
   p.d_bx = reinterpret_cast<Item*>(base + b_mats + b_k1 + b_syrk);
+  p.d_small = reinterpret_cast<int32_t*>(base + b_mats + b_k1 + b_syrk + b_bx);
   std::vector<char> host(total, 0);
   std::memcpy(host.data(), p.mats.data(), p.mats.size() * sizeof(MatDev));
   std::memcpy(host.data() + b_mats, p.k1_items.data(), p.k1_items.size() * sizeof(Item));
   std::memcpy(host.data() + b_mats + b_k1, p.syrk_items.data(), p.syrk_items.size() * sizeof(Item));
   std::memcpy(host.data() + b_mats + b_k1 + b_syrk, p.bx_items.data(),
               p.bx_items.size() * sizeof(Item));
+  std::memcpy(host.data() + b_mats + b_k1 + b_syrk + b_bx, p.small_list.data(),
+              p.small_list.size() * sizeof(int32_t));
   e = hipMemcpy(p.d_tables, host.data(), total, hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy(plan tables)");
   return MUON_OK;
@@ -412,21 +431,22 @@ int muon_workspace_size(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_
   if (workspace_bytes == nullptr) return fail(MUON_ERR_INVALID_ARG, "workspace_bytes is null");
   muon_plan p;
   const int rc = build_plan(mats, n_mats, flat_numel, param_dtype, grad_dtype, ns_dtype,
-                            workspace_cap, p);
+                            workspace_cap, 0u, p);
   if (rc != MUON_OK) return rc;
   *workspace_bytes = p.ws_bytes;
   return MUON_OK;
 }
 
-int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
-                     int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
-                     size_t workspace_cap, muon_plan_t** out, size_t* workspace_bytes) {
+int muon_plan_create_ex(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
+                        int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
+                        size_t workspace_cap, uint32_t flags, muon_plan_t** out,
+                        size_t* workspace_bytes) {
   if (out == nullptr) return fail(MUON_ERR_INVALID_ARG, "out is null");
   *out = nullptr;
   muon_plan* p = new (std::nothrow) muon_plan();
   if (p == nullptr) return fail(MUON_ERR_INVALID_ARG, "out of host memory");
   int rc = build_plan(mats, n_mats, flat_numel, param_dtype, grad_dtype, ns_dtype,
-                      workspace_cap, *p);
+                      workspace_cap, flags, *p);
   if (rc == MUON_OK) rc = upload_plan(*p);
   if (rc != MUON_OK) {
     muon_plan_destroy(p);
@@ -435,6 +455,13 @@ int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_num
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
   *out = p;
   return MUON_OK;
+}
+
+int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
+                     int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
+                     size_t workspace_cap, muon_plan_t** out, size_t* workspace_bytes) {
+  return muon_plan_create_ex(mats, n_mats, flat_numel, param_dtype, grad_dtype, ns_dtype,
+                             workspace_cap, 0u, out, workspace_bytes);
 }
 
 void muon_plan_destroy(muon_plan_t* plan) {
@@ -463,6 +490,7 @@ int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {
   info->bx_tiles = static_cast<int64_t>(plan->bx_items.size());
   info->workspace_bytes = plan->ws_bytes;
   info->ns_flops_per_iter_alg = plan->flops_per_iter;
+  info->small_mats = static_cast<int32_t>(plan->small_list.size());
   return MUON_OK;
 }
 
@@ -489,6 +517,31 @@ int muon_stage_momentum(const muon_plan_t* plan, int32_t wave, const void* grads
   return MUON_OK;
 }
 
+namespace {
+
+// Phase `phase` of NS iteration `iter` for the wave's tiled matrices; with
+// small_iters > 0 (phase 3 only) also small_iters whole iterations of its
+// small matrices, starting at `iter`.
+int run_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
+                 const muon_hparams_t* hp, int32_t iter, int32_t phase, int32_t small_iters,
+                 hipStream_t stream) {
+  const Wave& w = plan->waves[wave];
+  const Item* items = phase == 3 ? plan->d_bx + w.bx_begin : plan->d_syrk + w.syrk_begin;
+  const int n = static_cast<int>(phase == 3 ? w.bx_count : w.syrk_count);
+  muon::GemmArgs g = gemm_args(plan, w, workspace, hp, iter, items);
+  g.n_items = n;
+  hipError_t e = muon::launch_ns_phase(plan->ns_dtype, phase, n, plan->n_cu, g, stream);
+  if (e != hipSuccess) return hip_fail(e, "NS kernel launch");
+  if (small_iters > 0 && w.small_count > 0) {
+    e = muon::launch_ns_small(static_cast<int>(w.small_count), plan->d_small + w.small_begin,
+                              small_iters, g, stream);
+    if (e != hipSuccess) return hip_fail(e, "small-matrix NS kernel launch");
+  }
+  return MUON_OK;
+}
+
+}  // namespace
+
 int muon_stage_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
                         size_t workspace_bytes, const muon_hparams_t* hp, int32_t iter,
                         int32_t phase, hipStream_t stream) {
@@ -499,14 +552,8 @@ int muon_stage_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
   if (phase < 1 || phase > 3) return fail(MUON_ERR_INVALID_ARG, "phase must be 1, 2 or 3");
   if (phase == 2 && hp->ns_c == 0.0f)
     return fail(MUON_ERR_INVALID_ARG, "phase 2 is skipped when ns_c == 0");
-  const Wave& w = plan->waves[wave];
-  const Item* items = phase == 3 ? plan->d_bx + w.bx_begin : plan->d_syrk + w.syrk_begin;
-  const int n = static_cast<int>(phase == 3 ? w.bx_count : w.syrk_count);
-  muon::GemmArgs g = gemm_args(plan, w, workspace, hp, iter, items);
-  g.n_items = n;
-  const hipError_t e = muon::launch_ns_phase(plan->ns_dtype, phase, n, plan->n_cu, g, stream);
-  if (e != hipSuccess) return hip_fail(e, "NS kernel launch");
-  return MUON_OK;
+  // the small matrices run their whole iteration with phase 3
+  return run_ns_phase(plan, wave, workspace, hp, iter, phase, phase == 3 ? 1 : 0, stream);
 }
 
 int muon_stage_apply(const muon_plan_t* plan, int32_t wave, void* params, void* workspace,
@@ -568,12 +615,14 @@ int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* m
   for (int32_t w = 0; w < static_cast<int32_t>(plan->waves.size()); ++w) {
     rc = muon_stage_momentum(plan, w, grads, momentum, workspace, workspace_bytes, hp, stream);
     if (rc != MUON_OK) return rc;
+    // tiled matrices phase by phase; the small matrices run all their
+    // iterations in one launch (bitwise the same as one per iteration)
     for (int32_t it = 0; it < hp->ns_steps; ++it) {
-      rc = muon_stage_ns_phase(plan, w, workspace, workspace_bytes, hp, it, 1, stream);
+      rc = run_ns_phase(plan, w, workspace, hp, it, 1, 0, stream);
       if (rc == MUON_OK && hp->ns_c != 0.0f)
-        rc = muon_stage_ns_phase(plan, w, workspace, workspace_bytes, hp, it, 2, stream);
+        rc = run_ns_phase(plan, w, workspace, hp, it, 2, 0, stream);
       if (rc == MUON_OK)
-        rc = muon_stage_ns_phase(plan, w, workspace, workspace_bytes, hp, it, 3, stream);
+        rc = run_ns_phase(plan, w, workspace, hp, it, 3, it == 0 ? hp->ns_steps : 0, stream);
       if (rc != MUON_OK) return rc;
     }
     rc = muon_stage_apply(plan, w, params, workspace, workspace_bytes, hp, out_update, stream);

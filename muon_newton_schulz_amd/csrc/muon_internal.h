@@ -14,6 +14,10 @@ constexpr int kEwTile = 64;
 constexpr int kTileBf16 = 256;
 constexpr int kTileFp32 = 64;
 constexpr int kNsKStep = 32;  // bf16 engine: K per pipeline stage
+// Small matrices (bf16 NS): m_k <= kSmallM and m_k * n_k <= kSmallElems run
+// one NS iteration per launch in one workgroup, entirely in LDS.
+constexpr int kSmallM = 128;
+constexpr int kSmallElems = 32768;
 
 // One matrix of a plan, as the device sees it.  "Oriented" dims put the
 // short side first (m = min(rows, cols), n = max(rows, cols)); tall
@@ -30,6 +34,8 @@ struct MatDev {
   int32_t widx;          // index of the matrix within its wave
   int32_t k1_begin;      // first elementwise tile of this matrix (wave-local)
   int32_t k1_count;      // number of elementwise tiles of this matrix
+  int32_t small;         // 1: NS runs in the fused one-workgroup kernel
+  int32_t reserved;
   // element offsets (in NS elements) into the workspace
   int64_t ws_x[2];       // X : m_pad x n_pad, ping-pong
   int64_t ws_a;          // A : m_pad x m_pad
@@ -83,6 +89,10 @@ hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int
                          const void* ws, int x_idx, float* out, hipStream_t s);
 hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
                            const GemmArgs& args, hipStream_t s);
+// n_iter NS iterations (all phases) of each listed small matrix, starting
+// at the iteration args describes
+hipError_t launch_ns_small(int n_mats, const int32_t* list, int n_iter, const GemmArgs& args,
+                           hipStream_t s);
 // m_dtype: 0 fp32, 1 bf16; v_dtype: 0 fp32, 1 bf16, 2 fp16
 hipError_t launch_adamw(void* params, int param_dtype, float* master, const void* grads,
                         int grad_dtype, void* m, int m_dtype, void* v, int v_dtype, int64_t n,

@@ -53,7 +53,7 @@ class Setup:
     """Flat buffers + plan + workspace for a list of (offset, rows, cols)."""
 
     def __init__(self, mats, n, param_dtype, grad_dtype, ns_dtype, dev, seed=0,
-                 w_std=1.0, g_std=1.0, cap=0, sentinel=True):
+                 w_std=1.0, g_std=1.0, cap=0, sentinel=True, tiled_only=False):
         self.mats, self.n = mats, n
         self.param_dtype, self.ns_dtype = param_dtype, ns_dtype
         g = torch.Generator(device=dev)
@@ -68,7 +68,8 @@ class Setup:
             self.grads[o:o + r * c] = (torch.randn(r * c, generator=g, device=dev) * g_std).to(
                 self.grads.dtype)
             self.mom[o:o + r * c] = 0.0
-        self.plan = M.muon_plan_create(mats, n, param_dtype, grad_dtype, ns_dtype, cap)
+        self.plan = M.muon_plan_create(mats, n, param_dtype, grad_dtype, ns_dtype, cap,
+                                       tiled_only=tiled_only)
         self.ws = self.plan.alloc_workspace(dev)
         self.out = torch.full((n,), fill, dtype=torch.float32, device=dev)
 
@@ -244,6 +245,36 @@ def test_muon_vector_paths_aligned_ragged(gpu, ns_dtype, pdt):
     assert all(o % 4 == 0 and c % 4 == 0 for o, r, c in mats)
     s = Setup(mats, n, pdt, pdt, ns_dtype, gpu, seed=4)
     check_muon_step(s, mhp(QUINTIC), tol_w=1e-2 if pdt == "bf16" else 1e-4)
+
+
+# small matrices (short side padded to 32 at most 128, m_k * n_k <= 32768)
+# run one NS iteration per launch in one workgroup; mixed with tiled ones
+SMALL_SHAPES = [(128, 256), (256, 128), (96, 200), (200, 96), (17, 300), (1, 8), (32, 1000),
+                (64, 64), (100, 320), (300, 520), (129, 200)]
+
+
+@pytest.mark.parametrize("coef", [QUINTIC, CUBIC])
+@pytest.mark.parametrize("pdt", ["bf16", "fp32"])
+def test_small_matrix_kernel_is_bitwise_the_tiled_path(gpu, coef, pdt):
+    mats, n = _flat(SMALL_SHAPES)
+    fused = Setup(mats, n, pdt, pdt, "bf16", gpu, seed=8)
+    tiled = Setup(mats, n, pdt, pdt, "bf16", gpu, seed=8, tiled_only=True)
+    # (100, 320): m_k * n_k = 128 * 320 > 32768; (300, 520), (129, 200): m_k > 128
+    assert fused.plan.info().small_mats == 8 and tiled.plan.info().small_mats == 0
+    hp = mhp(coef)
+    for _ in range(2):  # two steps: the second starts from a nonzero momentum
+        fused.step(hp)
+        tiled.step(hp)
+    torch.cuda.synchronize()
+    for a, b in ((fused.params, tiled.params), (fused.mom, tiled.mom), (fused.out, tiled.out)):
+        assert torch.equal(a, b)
+
+
+def test_small_matrices_match_oracle(gpu):
+    mats, n = _flat(SMALL_SHAPES[:8])
+    s = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=12)
+    assert s.plan.info().small_mats == 8
+    check_muon_step(s, mhp(QUINTIC), tol_w=1e-2)
 
 
 def test_grouped_equals_single_matrix_plans(gpu):
