@@ -182,9 +182,10 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     d.n_pad = static_cast<int32_t>(round_up(std::max(d.rows, d.cols), T));
     d.m_k = static_cast<int32_t>(round_up(std::min(d.rows, d.cols), muon::kNsKStep));
     d.n_k = static_cast<int32_t>(round_up(std::max(d.rows, d.cols), muon::kNsKStep));
+    // small: m_k <= 128 and (m_k / 32) * ceil(n_k / 128) <= 8 (the fused
+    // kernel's register tiling; implies m_k * n_k <= 32768)
     d.small = (ns_dtype == MUON_DTYPE_BF16 && !(flags & MUON_PLAN_TILED_ONLY) &&
-               d.m_k <= muon::kSmallM &&
-               static_cast<int64_t>(d.m_k) * d.n_k <= muon::kSmallElems)
+               d.m_k <= muon::kSmallM && (d.m_k / 32) * ((d.n_k + 127) / 128) <= 8)
                   ? 1
                   : 0;
     const double m = std::min(d.rows, d.cols), n = std::max(d.rows, d.cols);

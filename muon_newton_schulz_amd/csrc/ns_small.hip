@@ -42,42 +42,48 @@ __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 
 // of accumulator register r, as in the tiled engine.
 
 // Fragment reads run one 16-wide k step ahead of the MFMAs (the k loop is
-// unrolled by two, K being a multiple of 32).  A wave with fewer blocks than
-// slots runs its spare slots on block 0's fragments and discards them, so
-// the loop has no branches.
+// unrolled by two, K being a multiple of 32), and every fragment read feeds
+// several MFMAs.  Slots a wave does not own run on block 0's fragments and
+// are discarded, so the k loop has no branches.
 
 // C = sc * P P^T (+ bterm * A, phase 2) (+ dval on the diagonal of the
 // diagonal blocks), rounded to bf16.  P: [rows][ld] bf16 in LDS, K-contiguous.
+// Wave (wr, wc) = (wave / 2, wave % 2) owns the 2 x 2 blocks bi = 2 wr + u,
+// bj = 2 wc + v (those inside the nb x nb grid): 2 P and 2 Q fragments per
+// k step for 4 MFMAs.
 template <bool ATERM>
 __device__ __forceinline__ void small_nt(const uint16_t* P, int ld, int K, int nb, float sc,
                                          float bterm, const uint16_t* A, float dval,
                                          uint16_t* C, int ldc, int wave, int lane) {
-  constexpr int NS = 4;
   const int frow = lane & 31, kh = (lane >> 5) * 8;
-  const int nblk = nb * nb;
-  int pa[NS], qa[NS];
+  const int wr = wave >> 1, wc = wave & 1;
+  int pa[2], qa[2];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int b = wave + 4 * s < nblk ? wave + 4 * s : 0;
-    const int bi = b / nb, bj = b - bi * nb;
-    pa[s] = (bi * 32 + frow) * ld + kh;
-    qa[s] = (bj * 32 + frow) * ld + kh;
+  for (int u = 0; u < 2; ++u) {
+    const int bi = 2 * wr + u < nb ? 2 * wr + u : 0;
+    const int bj = 2 * wc + u < nb ? 2 * wc + u : 0;
+    pa[u] = (bi * 32 + frow) * ld + kh;
+    qa[u] = (bj * 32 + frow) * ld + kh;
   }
-  f32x16_t acc[NS];
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) acc[s] = f32x16_t{};
-  bf16x8_t p0[NS], q0[NS], p1[NS], q1[NS];
-  auto load = [&](bf16x8_t (&pf)[NS], bf16x8_t (&qf)[NS], int k0) {
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      pf[s] = *reinterpret_cast<const bf16x8_t*>(P + pa[s] + k0);
-      qf[s] = *reinterpret_cast<const bf16x8_t*>(P + qa[s] + k0);
+    for (int v = 0; v < 2; ++v) acc[u][v] = f32x16_t{};
+  bf16x8_t p0[2], q0[2], p1[2], q1[2];
+  auto load = [&](bf16x8_t (&pf)[2], bf16x8_t (&qf)[2], int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      pf[u] = *reinterpret_cast<const bf16x8_t*>(P + pa[u] + k0);
+      qf[u] = *reinterpret_cast<const bf16x8_t*>(P + qa[u] + k0);
     }
   };
-  auto mma = [&](const bf16x8_t (&pf)[NS], const bf16x8_t (&qf)[NS]) {
+  auto mma = [&](const bf16x8_t (&pf)[2], const bf16x8_t (&qf)[2]) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], pf[s], acc[s], 0, 0, 0);
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+        acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[v], pf[u], acc[u][v], 0, 0, 0);
   };
   load(p0, q0, 0);
   for (int k0 = 0; k0 < K; k0 += 32) {
@@ -88,72 +94,81 @@ __device__ __forceinline__ void small_nt(const uint16_t* P, int ld, int K, int n
   }
   // four consecutive columns per lane and register group: 8-byte accesses
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int b = wave + 4 * s;
-    if (b < nblk) {
-      const int bi = b / nb, bj = b - bi * nb;
-      const int i = bi * 32 + frow;
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j0 = bj * 32 + 8 * q + 4 * (lane >> 5);
-        float v[4];
+    for (int v = 0; v < 2; ++v) {
+      const int bi = 2 * wr + u, bj = 2 * wc + v;
+      if (bi < nb && bj < nb) {
+        const int i = bi * 32 + frow;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = sc * acc[s][4 * q + e];
-        if constexpr (ATERM) {
-          const u32x2_t a = *reinterpret_cast<const u32x2_t*>(A + i * ldc + j0);
-          v[0] += bterm * lo_bf(a[0]);
-          v[1] += bterm * hi_bf(a[0]);
-          v[2] += bterm * lo_bf(a[1]);
-          v[3] += bterm * hi_bf(a[1]);
+        for (int q = 0; q < 4; ++q) {
+          const int j0 = bj * 32 + 8 * q + 4 * (lane >> 5);
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = sc * acc[u][v][4 * q + e];
+          if constexpr (ATERM) {
+            const u32x2_t a = *reinterpret_cast<const u32x2_t*>(A + i * ldc + j0);
+            x[0] += bterm * lo_bf(a[0]);
+            x[1] += bterm * hi_bf(a[0]);
+            x[2] += bterm * lo_bf(a[1]);
+            x[3] += bterm * hi_bf(a[1]);
+          }
+          if (bi == bj) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] += i == j0 + e ? dval : 0.0f;
+          }
+          *reinterpret_cast<u32x2_t*>(C + i * ldc + j0) =
+              u32x2_t{pack2(x[0], x[1]), pack2(x[2], x[3])};
         }
-        if (bi == bj) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += i == j0 + e ? dval : 0.0f;
-        }
-        *reinterpret_cast<u32x2_t*>(C + i * ldc + j0) = u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])};
       }
     }
-  }
 }
 
-// X <- sc * (B X) in LDS: B [mk][ldb], X [mk][ldx].  The X fragments (8
-// consecutive k of one column) come from two ds_read_b64_tr_b16: each
-// 16-lane group reads a 4 x 16 block (lane s: row s/4, columns 4*(s%4)..+3)
-// and every lane receives one column's 4 rows.
+// X <- sc * (B X) in LDS: B [mk][ldb], X [mk][ldx], NU = mk / 32 row blocks.
+// Wave w owns every row block and the column blocks bj = w + 4 t, t < NT:
+// NU B fragments and NT X fragments per k step for NU * NT MFMAs.  The X
+// fragments (8 consecutive k of one column) come from two
+// ds_read_b64_tr_b16: each 16-lane group reads a 4 x 16 block (lane s: row
+// s/4, columns 4*(s%4)..+3) and every lane receives one column's 4 rows.
+template <int NU, int NT>
 __device__ __forceinline__ void small_bx(const uint16_t* B, int ldb, uint16_t* X, int ldx, int mk,
                                          int nk, float sc, int wave, int lane) {
-  constexpr int NS = 8;
   const int frow = lane & 31, kh = (lane >> 5) * 8;
   const int ts = lane & 15;
   const int trow = kh + (ts >> 2), tcol = 16 * ((lane >> 4) & 1) + 4 * (ts & 3);
-  const int nbn = nk >> 5, nblk = (mk >> 5) * nbn;
-  int ba[NS], xa[NS];
+  const int nbn = nk >> 5;
+  int ba[NU], xa[NT];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int b = wave + 4 * s < nblk ? wave + 4 * s : 0;
-    const int bi = b / nbn, bj = b - bi * nbn;
-    ba[s] = (bi * 32 + frow) * ldb + kh;
-    xa[s] = trow * ldx + bj * 32 + tcol;
+  for (int u = 0; u < NU; ++u) ba[u] = (u * 32 + frow) * ldb + kh;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int bj = wave + 4 * t < nbn ? wave + 4 * t : 0;
+    xa[t] = trow * ldx + bj * 32 + tcol;
   }
-  f32x16_t acc[NS];
+  f32x16_t acc[NU][NT];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) acc[s] = f32x16_t{};
-  bf16x8_t p0[NS], q0[NS], p1[NS], q1[NS];
-  auto load = [&](bf16x8_t (&pf)[NS], bf16x8_t (&qf)[NS], int k0) {
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      pf[s] = *reinterpret_cast<const bf16x8_t*>(B + ba[s] + k0);
-      const uint16_t* x = X + xa[s] + k0 * ldx;
+    for (int t = 0; t < NT; ++t) acc[u][t] = f32x16_t{};
+  bf16x8_t p0[NU], q0[NT], p1[NU], q1[NT];
+  auto load = [&](bf16x8_t (&pf)[NU], bf16x8_t (&qf)[NT], int k0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) pf[u] = *reinterpret_cast<const bf16x8_t*>(B + ba[u] + k0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint16_t* x = X + xa[t] + k0 * ldx;
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(x));
       const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(x + 4 * ldx));
-      qf[s] = __builtin_bit_cast(bf16x8_t,
+      qf[t] = __builtin_bit_cast(bf16x8_t,
                                  __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
-  auto mma = [&](const bf16x8_t (&pf)[NS], const bf16x8_t (&qf)[NS]) {
+  auto mma = [&](const bf16x8_t (&pf)[NU], const bf16x8_t (&qf)[NT]) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], pf[s], acc[s], 0, 0, 0);
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t], pf[u], acc[u][t], 0, 0, 0);
   };
   load(p0, q0, 0);
   for (int k0 = 0; k0 < mk; k0 += 32) {
@@ -164,19 +179,31 @@ __device__ __forceinline__ void small_bx(const uint16_t* B, int ldb, uint16_t* X
   }
   __syncthreads();  // every wave is done reading X
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int b = wave + 4 * s;
-    if (b < nblk) {
-      const int bi = b / nbn, bj = b - bi * nbn;
-      const int i = bi * 32 + frow;
+  for (int t = 0; t < NT; ++t) {
+    const int bj = wave + 4 * t;
+    if (bj < nbn) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j0 = bj * 32 + 8 * q + 4 * (lane >> 5);
-        *reinterpret_cast<u32x2_t*>(X + i * ldx + j0) =
-            u32x2_t{pack2(sc * acc[s][4 * q], sc * acc[s][4 * q + 1]),
-                    pack2(sc * acc[s][4 * q + 2], sc * acc[s][4 * q + 3])};
+      for (int u = 0; u < NU; ++u) {
+        const int i = u * 32 + frow;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j0 = bj * 32 + 8 * q + 4 * (lane >> 5);
+          *reinterpret_cast<u32x2_t*>(X + i * ldx + j0) =
+              u32x2_t{pack2(sc * acc[u][t][4 * q], sc * acc[u][t][4 * q + 1]),
+                      pack2(sc * acc[u][t][4 * q + 2], sc * acc[u][t][4 * q + 3])};
+        }
       }
     }
+  }
+}
+
+__device__ __forceinline__ void small_bx_any(const uint16_t* B, int ldb, uint16_t* X, int ldx,
+                                             int mk, int nk, float sc, int wave, int lane) {
+  switch (mk >> 5) {  // the host admits nb * ceil(nbn / 4) <= 8
+    case 1: small_bx<1, 8>(B, ldb, X, ldx, mk, nk, sc, wave, lane); break;
+    case 2: small_bx<2, 4>(B, ldb, X, ldx, mk, nk, sc, wave, lane); break;
+    case 3: small_bx<3, 2>(B, ldb, X, ldx, mk, nk, sc, wave, lane); break;
+    default: small_bx<4, 2>(B, ldb, X, ldx, mk, nk, sc, wave, lane); break;
   }
 }
 
@@ -233,7 +260,7 @@ __global__ __launch_bounds__(256) void k_ns_small(GemmArgs g, const int32_t* __r
                       lane);
     }
     __syncthreads();
-    small_bx(sb, lda, sx, ldx, mk, nk, inv, wave, lane);
+    small_bx_any(sb, lda, sx, ldx, mk, nk, inv, wave, lane);
     __syncthreads();
   }
   __syncthreads();
