@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ns_gemm_dense_d2048_l16_traffic.md")
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "ns_gemm_dense_d2048_l16_mfma.md")
 NS_SOURCE = os.path.join(ROOT, "muon_newton_schulz_amd", "csrc", "ns_gemm.hip")
 
 
@@ -44,6 +45,23 @@ def measured_traffic(workload):
     if data.get("ns_gemm_hip_sha256") != sha or data.get("workload") != workload:
         return None
     return data["fetch_bytes_per_launch"] + data["write_bytes_per_launch"]
+
+
+def measured_mfma_util(workload):
+    """rocprofv3 MfmaUtil (MFMA-busy cycles per SIMD over active cycles, in
+    %) of each NS kernel from the committed counter summary, or None when
+    it is missing, is for another workload, or was taken on a different
+    kernel source."""
+    import hashlib
+    try:
+        text = open(MFMA_SUMMARY).read()
+        data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        sha = hashlib.sha256(open(NS_SOURCE, "rb").read()).hexdigest()
+    except (OSError, IndexError, ValueError):
+        return None
+    if data.get("ns_gemm_hip_sha256") != sha or data.get("workload") != workload:
+        return None
+    return {k: round(v["mfma_util_pct"], 1) for k, v in data["kernels"].items()}
 
 
 def mfma_ceiling():
@@ -404,6 +422,9 @@ def main():
             # power management), measured after the timed region
             "sustained_mfma_ceiling": ceiling,
             "frac_of_sustained_ceiling": (f3_tflops / ceiling["tflops"]) if ceiling else None,
+            # rocprofv3 MfmaUtil of each NS kernel (counter summary under
+            # profiles/, null once the kernel source has changed)
+            "mfma_busy_pct": measured_mfma_util(args.workload),
         },
         "breakdown_ms_per_step": {
             "momentum+norm": k["momentum"][0] * k["momentum"][1],
