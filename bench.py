@@ -151,7 +151,7 @@ def cpu_baseline(wl, hp, sample_mats, adam_n):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the optimizer step runs on one GPU only; --gpus must be 1 "
                           "(the path shards by whole matrices across GPUs, not implemented)"}))
         sys.exit(2)
 
