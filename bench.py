@@ -459,9 +459,9 @@ def main():
         "muon_clip": muon_clip,
     }
     if not args.no_cpu_baseline:
-        # first layer of the stack: 4 square + 3 rectangular matrices
-        sample = list(range(7)) if len(shapes) >= 7 else list(range(len(shapes)))
-        result["cpu_baseline"] = cpu_baseline(wl, hp, sample, 1 << 22)
+        # the first three layers of the stack: 12 square + 9 rectangular matrices
+        sample = list(range(min(21, len(shapes))))
+        result["cpu_baseline"] = cpu_baseline(wl, hp, sample, 1 << 23)
     print(json.dumps(result), flush=True)
 
 
