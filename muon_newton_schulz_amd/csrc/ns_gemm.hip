@@ -183,10 +183,24 @@ __device__ __forceinline__ int stg(int i, int j) {
   return i * 128 + ((((j >> 2) ^ g) & 31) << 2);
 }
 
+// Diagonal tiles of the symmetric products (phases 1, 2) need only the 36
+// upper 32x32 blocks of their 8x8.  ROLE 1, waves (0,0) and (1,1): the upper
+// blocks of their quadrant (bi <= bj, 10 of 16).  ROLE 2: wave (0,1) the left
+// half of quadrant (0,1) (bj < 2, 8 blocks), wave (1,0) the same on Q rows
+// 64 further, i.e. that quadrant's right half.  Every wave writes its blocks
+// and, mirrored, their transposes, so a diagonal tile costs 10 MFMA slots
+// per substep instead of 16.  ROLE 0: the whole quadrant (every other tile).
+__device__ __forceinline__ int tile_role(int phase, int ti, int tj, int wave) {
+  if (phase == 3 || ti != tj) return 0;
+  return (wave == 0 || wave == 3) ? 1 : 2;
+}
+
 // One 256x256 output tile: operand pipeline, MFMA main loop, epilogue.
-template <int PHASE>
+template <int PHASE, int ROLE>
 __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, const int ti,
                                         const int tj, const float inv, uint16_t* smem) {
+  // MFMA m = 4 bj + bi runs iff bit m is set
+  constexpr uint32_t MASK = ROLE == 1 ? 0xF731u : ROLE == 2 ? 0x00FFu : 0xFFFFu;
   uint16_t* ws = static_cast<uint16_t*>(g.ws);
 
   // operands
@@ -216,6 +230,11 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wi = wave & 1, wj = wave >> 1;
   const int frow = lane & 31;
+  // quadrant this wave computes (wave (1,0) of a diagonal tile: quadrant
+  // (0,1), Q rows shifted by 64)
+  const bool adopt = ROLE == 2 && wi == 1;
+  const int wie = adopt ? 0 : wi, wje = adopt ? 1 : wj;
+  const int qshift = adopt ? 64 : 0;
 
   // MFMA operand fragments.  A fragment set (one 16-wide k substep) is
   // NR LDS reads: 4 P fragments (ds_read_b128) then the Q fragments, 4
@@ -231,8 +250,8 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int sw = ((ks * 2 + (lane >> 5)) ^ ((frow >> 2) & 3)) << 3;
-    vp[ks] = ((wi * 128 + frow) * BK + sw) * 2;
-    vq[ks] = BT * BK * 2 + ((wj * 128 + frow) * BK + sw) * 2;
+    vp[ks] = ((wie * 128 + frow) * BK + sw) * 2;
+    vq[ks] = BT * BK * 2 + ((wje * 128 + qshift + frow) * BK + sw) * 2;
   }
   // phase 3: transposed reads of column block b.  Lane group of 16: k row
   // 8*(lane/32) + (lane%16)/4 (+4 for the hi half, +16 per substep), columns
@@ -256,7 +275,10 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     if constexpr (R < 4) {
       f.p[R] = ld128_async<R * 32 * BK * 2>(vp[KS] + sb);
     } else if constexpr (PHASE != 3) {
-      f.q[R - 4] = ld128_async<(R - 4) * 32 * BK * 2>(vq[KS] + sb);
+      // ROLE 2 uses Q fragments 0 and 1 only (the others would lie past
+      // the shifted wave's Q rows)
+      if constexpr (ROLE != 2 || R - 4 < 2)
+        f.q[R - 4] = ld128_async<(R - 4) * 32 * BK * 2>(vq[KS] + sb);
     } else {
       constexpr int B = (R - 4) >> 1, H = (R - 4) & 1;
       f.t[R - 4] = ld_tr_async<KS * 16 * BT * 2 + H * 4 * BT * 2>(vt[B] + sb);
@@ -343,8 +365,9 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, 16>([&](auto m_c) {
       constexpr int m = decltype(m_c)::value;
-      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          F[0].q[m >> 2], F[0].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+      if constexpr ((MASK >> m) & 1u)
+        acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            F[0].q[m >> 2], F[0].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
       if constexpr (m < NR) issue_read(F[1], sb, Int<1>{}, Int<m>{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -360,8 +383,9 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     const uint32_t nsb = lds0 + ((kt + 1) % NSLOT) * SLOT_BYTES;
     static_for<0, 16>([&](auto m_c) {
       constexpr int m = decltype(m_c)::value;
-      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          F[1].q[m >> 2], F[1].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+      if constexpr ((MASK >> m) & 1u)
+        acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            F[1].q[m >> 2], F[1].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
       // after MFMA m: DMA m/2 on even m, read m/2 on odd m, and reads
       // 8..NR-1 after MFMAs 8..NR-1
       if constexpr (REFILL && (m & 1) == 0) issue_dma(kt + NSLOT - 1, rslot, Int<(m >> 1)>{});
@@ -378,7 +402,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // Phase 2's epilogue adds b*A: this wave's 128x128 sub-tile of A is
   // loaded into registers while the last stage computes (16-byte row
   // loads: row lane/16 + 4u, 16-byte chunk lane%16).
-  const int i0w = ti * BT + wi * 128, j0w = tj * BT + wj * 128;
+  const int i0w = ti * BT + wie * 128, j0w = tj * BT + wje * 128 + qshift;
   constexpr bool aterm = PHASE == 2;
   u32x4_t apre[32];
   if constexpr (aterm) {
@@ -413,7 +437,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   } else {
     C = ws + ((PHASE == 1 && g.c != 0.0f) ? md.ws_a : md.ws_b);
     ldc = md.m_pad;
-    mirror = ti != tj;
+    mirror = true;  // off-diagonal tiles whole, diagonal tiles block by block
   }
 
   // Staging-layout addressing.  For the accumulator positions of this
@@ -479,15 +503,25 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     }
   __syncthreads();
 
-  // row stores: 16 bytes per lane, 4 rows of 256 bytes per instruction
+  // row stores: 16 bytes per lane, 4 rows of 256 bytes per instruction;
+  // ROLE 1 stores its upper blocks (block row r/32 <= block column rc/4),
+  // ROLE 2 staged columns 0..63 (j0w includes the Q shift)
 #pragma unroll 8
   for (int u = 0; u < 32; ++u) {
     const int r = (elane >> 4) + 4 * u;
+    if (ROLE == 1 && (r >> 5) > (rc >> 2)) continue;
+    if (ROLE == 2 && rc >= 8) continue;
     u32x4_t v = *reinterpret_cast<const u32x4_t*>(S + row_slot16(u));
     if (u & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
     *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(i0w + r) * ldc + j0w + 8 * rc) = v;
   }
 
+  // mirror piece u (rows 16*(u/4).., columns 32*(u%4).. of the staged
+  // tile: source block (u/8, u%4)) is written iff this wave computed it
+  // and, on a diagonal quadrant, it lies strictly above the diagonal
+  auto mirror_keep = [](int u) {
+    return ROLE == 0 || (ROLE == 1 ? (u >> 3) < (u & 3) : (u & 3) < 2);
+  };
   if (mirror) {
     // C^T[j][i..i+7] = C[i..i+7][j] via two transpose reads per lane:
     // group G = lane/16 covers columns jb + 16*(G&1) + (lane%16) and rows
@@ -500,6 +534,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const int u = u0 + v;
+        if (!mirror_keep(u)) continue;
         const int jb = (u & 3) * 32, ib = (u >> 2) * 16;
         const int ir = ib + 8 * (G >> 1) + (s >> 2);
         const int jc = jb + 16 * (G & 1) + 4 * (s & 3);
@@ -510,6 +545,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const int u = u0 + v;
+        if (!mirror_keep(u)) continue;
         const int jb = (u & 3) * 32, ib = (u >> 2) * 16;
         const int jo = jb + 16 * (G & 1) + s;
         const int io = ib + 8 * (G >> 1);
@@ -544,7 +580,11 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g, const Item* __re
     const float inv = g.first ? invs[md.widx] : 1.0f;
     if (busy) __syncthreads();  // the previous tile's epilogue is done with LDS
     busy = true;
-    ns_tile<PHASE>(g, md, it.rc >> 16, it.rc & 0xffff, inv, smem);
+    const int ti = it.rc >> 16, tj = it.rc & 0xffff;
+    const int role = tile_role(PHASE, ti, tj, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    if (PHASE != 3 && role == 1) ns_tile<PHASE, 1>(g, md, ti, tj, inv, smem);
+    else if (PHASE != 3 && role == 2) ns_tile<PHASE, 2>(g, md, ti, tj, inv, smem);
+    else ns_tile<PHASE, 0>(g, md, ti, tj, inv, smem);
   }
 }
 

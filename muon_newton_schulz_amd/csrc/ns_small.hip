@@ -47,7 +47,8 @@ __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 
 // are discarded, so the k loop has no branches.
 
 // C = sc * P P^T (+ bterm * A, phase 2) (+ dval on the diagonal of the
-// diagonal blocks), rounded to bf16.  P: [rows][ld] bf16 in LDS, K-contiguous.
+// diagonal blocks), rounded to bf16, for the blocks on and above the
+// diagonal.  P: [rows][ld] bf16 in LDS, K-contiguous.
 // Wave (wr, wc) = (wave / 2, wave % 2) owns the 2 x 2 blocks bi = 2 wr + u,
 // bj = 2 wc + v (those inside the nb x nb grid): 2 P and 2 Q fragments per
 // k step for 4 MFMAs.
@@ -92,13 +93,14 @@ __device__ __forceinline__ void small_nt(const uint16_t* P, int ld, int K, int n
     if (k0 + 32 < K) load(p0, q0, k0 + 32);
     mma(p1, q1);
   }
-  // four consecutive columns per lane and register group: 8-byte accesses
+  // four consecutive columns per lane and register group: 8-byte accesses;
+  // only the blocks on and above the diagonal (small_mirror fills the rest)
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       const int bi = 2 * wr + u, bj = 2 * wc + v;
-      if (bi < nb && bj < nb) {
+      if (bi < nb && bj < nb && bi <= bj) {
         const int i = bi * 32 + frow;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -122,6 +124,16 @@ __device__ __forceinline__ void small_nt(const uint16_t* P, int ld, int K, int n
         }
       }
     }
+}
+
+// As in the tiled engine's diagonal tile, the 32x32 blocks below the
+// diagonal are the transposes of those above it.  Every thread; between
+// barriers (the upper blocks are final, the lower ones not yet read).
+__device__ __forceinline__ void small_mirror(uint16_t* C, int ldc, int mk) {
+  for (int e = threadIdx.x; e < mk * mk; e += 256) {
+    const int i = e / mk, j = e - i * mk;
+    if ((i >> 5) > (j >> 5)) C[i * ldc + j] = C[j * ldc + i];
+  }
 }
 
 // X <- sc * (B X) in LDS: B [mk][ldb], X [mk][ldx], NU = mk / 32 row blocks.
@@ -254,11 +266,15 @@ __global__ __launch_bounds__(256) void k_ns_small(GemmArgs g, const int32_t* __r
       small_nt<false>(sx, ldx, nk, nb, g.e1_scale * s2, 0.0f, nullptr, g.e1_diag, sa, lda, wave,
                       lane);
       __syncthreads();
+      small_mirror(sa, lda, mk);
+      __syncthreads();
       small_nt<true>(sa, lda, mk, nb, g.e2_scale, g.b, sa, g.e2_diag, sb, lda, wave, lane);
     } else {
       small_nt<false>(sx, ldx, nk, nb, g.e1_scale * s2, 0.0f, nullptr, g.e1_diag, sb, lda, wave,
                       lane);
     }
+    __syncthreads();
+    small_mirror(sb, lda, mk);
     __syncthreads();
     small_bx_any(sb, lda, sx, ldx, mk, nk, inv, wave, lane);
     __syncthreads();
