@@ -146,7 +146,9 @@ typedef struct {
   size_t workspace_bytes;
   double ns_flops_per_iter_alg;   /* algorithmic flops per NS iteration with c != 0 */
   int32_t small_mats;         /* matrices on the fused small-matrix path (below) */
-  int32_t reserved;
+  int32_t split_diag_mats;    /* tiled bf16 matrices whose diagonal tiles of
+                                 X X^T and A A compute only their upper blocks
+                                 (below) */
 } muon_plan_info_t;
 
 /* Host-only sizing: validates exactly as muon_plan_create and returns the
@@ -169,8 +171,17 @@ int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_num
  * most 128 and whose m_k * n_k is at most 32768 runs each NS iteration in
  * one workgroup with X, A and B in LDS (one launch per iteration instead of
  * three single-tile launches); its iterates are bitwise those of the tiled
- * path.  MUON_PLAN_TILED_ONLY puts every matrix on the tiled path. */
+ * path.  MUON_PLAN_TILED_ONLY puts every matrix on the tiled path.
+ *
+ * X X^T and A A are symmetric: the tiled path computes the tiles on and
+ * above the diagonal and mirrors them.  On a tiled bf16 matrix whose short
+ * side pads to at most 8 tiles (2048), a diagonal tile also computes only
+ * its upper 32x32 blocks and mirrors the rest; larger matrices compute whole
+ * diagonal tiles (splitting them was measured slower there).  The result is
+ * bitwise the same either way; MUON_PLAN_FULL_DIAG computes whole diagonal
+ * tiles for every matrix. */
 #define MUON_PLAN_TILED_ONLY 1u
+#define MUON_PLAN_FULL_DIAG 2u
 int muon_plan_create_ex(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                         int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
                         size_t workspace_cap, uint32_t flags, muon_plan_t** out,

@@ -99,7 +99,7 @@ class MuonPlanInfo(ctypes.Structure):
                 ("k1_tiles", ctypes.c_int64), ("syrk_tiles", ctypes.c_int64),
                 ("bx_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("ns_flops_per_iter_alg", ctypes.c_double), ("small_mats", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("split_diag_mats", ctypes.c_int32)]
 
 
 _lib_handle = None
@@ -299,19 +299,23 @@ def muon_workspace_size(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype
 
 
 MUON_PLAN_TILED_ONLY = 1
+MUON_PLAN_FULL_DIAG = 2
 
 
 def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="bf16",
-                     workspace_cap: int = 0, tiled_only: bool = False) -> MuonPlan:
+                     workspace_cap: int = 0, tiled_only: bool = False,
+                     full_diag: bool = False) -> MuonPlan:
     """tiled_only: every matrix on the tiled NS path (no fused small-matrix
-    kernel); results are bitwise the same either way."""
+    kernel); full_diag: whole diagonal tiles in the symmetric products.
+    Results are bitwise the same either way."""
     arr = _mats_array(mats)
     h = ctypes.c_void_p(0)
     ws = ctypes.c_size_t(0)
     _check(lib().muon_plan_create_ex(arr, len(mats), int(flat_numel), dtype_code(param_dtype),
                                      dtype_code(grad_dtype), dtype_code(ns_dtype),
                                      int(workspace_cap),
-                                     MUON_PLAN_TILED_ONLY if tiled_only else 0,
+                                     (MUON_PLAN_TILED_ONLY if tiled_only else 0)
+                                     | (MUON_PLAN_FULL_DIAG if full_diag else 0),
                                      ctypes.byref(h), ctypes.byref(ws)))
     return MuonPlan(h.value, ws.value, len(mats), int(flat_numel), dtype_code(param_dtype),
                     dtype_code(grad_dtype))

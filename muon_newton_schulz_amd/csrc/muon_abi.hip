@@ -124,7 +124,7 @@ void emit_super_tiles(int mat, int rows, int cols, bool tri, std::vector<Item>& 
 int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype, size_t workspace_cap,
                uint32_t flags, muon_plan& p) {
-  if ((flags & ~static_cast<uint32_t>(MUON_PLAN_TILED_ONLY)) != 0)
+  if ((flags & ~static_cast<uint32_t>(MUON_PLAN_TILED_ONLY | MUON_PLAN_FULL_DIAG)) != 0)
     return fail(MUON_ERR_INVALID_ARG, "unknown plan flags");
   if (n_mats < 0) return fail(MUON_ERR_INVALID_ARG, "n_mats < 0");
   if (n_mats > 0 && mats == nullptr) return fail(MUON_ERR_INVALID_ARG, "mats is null");
@@ -188,6 +188,10 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                d.m_k <= muon::kSmallM && (d.m_k / 32) * ((d.n_k + 127) / 128) <= 8)
                   ? 1
                   : 0;
+    d.diag = (ns_dtype == MUON_DTYPE_BF16 && !d.small && !(flags & MUON_PLAN_FULL_DIAG) &&
+              d.m_pad / T <= muon::kDiagMaxTiles)
+                 ? 1
+                 : 0;
     const double m = std::min(d.rows, d.cols), n = std::max(d.rows, d.cols);
     p.flops_per_iter += m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n;
   }
@@ -492,6 +496,8 @@ int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {
   info->workspace_bytes = plan->ws_bytes;
   info->ns_flops_per_iter_alg = plan->flops_per_iter;
   info->small_mats = static_cast<int32_t>(plan->small_list.size());
+  info->split_diag_mats = 0;
+  for (const muon::MatDev& d : plan->mats) info->split_diag_mats += d.diag;
   return MUON_OK;
 }
 

@@ -18,6 +18,13 @@ constexpr int kNsKStep = 32;  // bf16 engine: K per pipeline stage
 // one NS iteration per launch in one workgroup, entirely in LDS.
 constexpr int kSmallM = 128;
 constexpr int kSmallElems = 32768;
+// Tiled bf16 NS: the diagonal tiles of A = X X^T and A A split their upper
+// blocks between the waves for matrices with at most this many tiles per
+// side of A (m_pad / kTileBf16); larger matrices compute full diagonal tiles.
+#ifndef MUON_DIAG_MAX_TILES
+#define MUON_DIAG_MAX_TILES 8
+#endif
+constexpr int kDiagMaxTiles = MUON_DIAG_MAX_TILES;
 
 // One matrix of a plan, as the device sees it.  "Oriented" dims put the
 // short side first (m = min(rows, cols), n = max(rows, cols)); tall
@@ -35,7 +42,8 @@ struct MatDev {
   int32_t k1_begin;      // first elementwise tile of this matrix (wave-local)
   int32_t k1_count;      // number of elementwise tiles of this matrix
   int32_t small;         // 1: NS runs in the fused one-workgroup kernel
-  int32_t reserved;
+  int32_t diag;          // 1: diagonal tiles of the symmetric products
+                         // compute only their upper blocks
   // element offsets (in NS elements) into the workspace
   int64_t ws_x[2];       // X : m_pad x n_pad, ping-pong
   int64_t ws_a;          // A : m_pad x m_pad

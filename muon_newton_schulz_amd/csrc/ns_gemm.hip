@@ -581,7 +581,8 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g, const Item* __re
     if (busy) __syncthreads();  // the previous tile's epilogue is done with LDS
     busy = true;
     const int ti = it.rc >> 16, tj = it.rc & 0xffff;
-    const int role = tile_role(PHASE, ti, tj, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    const int role =
+        md.diag ? tile_role(PHASE, ti, tj, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) : 0;
     if (PHASE != 3 && role == 1) ns_tile<PHASE, 1>(g, md, ti, tj, inv, smem);
     else if (PHASE != 3 && role == 2) ns_tile<PHASE, 2>(g, md, ti, tj, inv, smem);
     else ns_tile<PHASE, 0>(g, md, ti, tj, inv, smem);

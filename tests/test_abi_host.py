@@ -193,3 +193,20 @@ def test_clip_plan_validates_before_any_hip_call():
     assert L.muon_clip(None, fake, 0, 1.0, None, fake, 8, None, None, None) == \
         M.MUON_ERR_INVALID_ARG
     L.muon_clip_plan_destroy(None)  # a null plan is a no-op
+
+
+def test_plan_flags_validate_before_any_hip_call():
+    L = M.lib()
+    mats = (M.MuonMatrix * 1)(M.MuonMatrix(0, 8, 8))
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+
+    def rc(flags):
+        return L.muon_plan_create_ex(mats, 1, 64, 1, 1, 1, 0, flags, ctypes.byref(h),
+                                     ctypes.byref(ws))
+    assert M.MUON_PLAN_TILED_ONLY == 1 and M.MUON_PLAN_FULL_DIAG == 2
+    assert rc(4) == M.MUON_ERR_INVALID_ARG
+    assert rc(1 << 31) == M.MUON_ERR_INVALID_ARG
+    # the known flags pass validation and the call gets as far as the device
+    for f in (0, 1, 2, 3):
+        assert rc(f) not in (M.MUON_ERR_INVALID_ARG, M.MUON_ERR_BAD_SHAPE, M.MUON_ERR_BAD_DTYPE)

@@ -53,7 +53,8 @@ class Setup:
     """Flat buffers + plan + workspace for a list of (offset, rows, cols)."""
 
     def __init__(self, mats, n, param_dtype, grad_dtype, ns_dtype, dev, seed=0,
-                 w_std=1.0, g_std=1.0, cap=0, sentinel=True, tiled_only=False):
+                 w_std=1.0, g_std=1.0, cap=0, sentinel=True, tiled_only=False,
+                 full_diag=False):
         self.mats, self.n = mats, n
         self.param_dtype, self.ns_dtype = param_dtype, ns_dtype
         g = torch.Generator(device=dev)
@@ -69,7 +70,7 @@ class Setup:
                 self.grads.dtype)
             self.mom[o:o + r * c] = 0.0
         self.plan = M.muon_plan_create(mats, n, param_dtype, grad_dtype, ns_dtype, cap,
-                                       tiled_only=tiled_only)
+                                       tiled_only=tiled_only, full_diag=full_diag)
         self.ws = self.plan.alloc_workspace(dev)
         self.out = torch.full((n,), fill, dtype=torch.float32, device=dev)
 
@@ -267,6 +268,29 @@ def test_small_matrix_kernel_is_bitwise_the_tiled_path(gpu, coef, pdt):
         tiled.step(hp)
     torch.cuda.synchronize()
     for a, b in ((fused.params, tiled.params), (fused.mom, tiled.mom), (fused.out, tiled.out)):
+        assert torch.equal(a, b)
+
+
+# diagonal tiles of the symmetric products split into upper blocks for a
+# short side padded to at most 8 tiles (2048); (2304, 2400) has 9 and
+# computes whole diagonal tiles either way; (64, 64) is on the fused path
+DIAG_SHAPES = [(2048, 2100), (2100, 2048), (300, 520), (520, 300), (1000, 700), (2304, 2400),
+               (64, 64)]
+
+
+@pytest.mark.parametrize("coef", [QUINTIC, CUBIC])
+def test_split_diagonal_tiles_are_bitwise_whole_tiles(gpu, coef):
+    mats, n = _flat(DIAG_SHAPES)
+    split = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=14)
+    whole = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=14, full_diag=True)
+    assert split.plan.info().split_diag_mats == 5 and whole.plan.info().split_diag_mats == 0
+    assert split.plan.info().small_mats == 1
+    hp = mhp(coef)
+    for _ in range(2):
+        split.step(hp)
+        whole.step(hp)
+    torch.cuda.synchronize()
+    for a, b in ((split.params, whole.params), (split.mom, whole.mom), (split.out, whole.out)):
         assert torch.equal(a, b)
 
 
