@@ -27,22 +27,33 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ns_gemm_dense_d2048_l16_traffic.md")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "ns_gemm_dense_d2048_l16_mfma.md")
-NS_SOURCE = os.path.join(ROOT, "muon_newton_schulz_amd", "csrc", "ns_gemm.hip")
+# the NS kernels are compiled from these two files
+NS_SOURCES = [os.path.join(ROOT, "muon_newton_schulz_amd", "csrc", f)
+              for f in ("ns_gemm.hip", "muon_internal.h")]
+
+
+def ns_source_sha256():
+    """sha256 over the NS kernels' source files, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in NS_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary, or None when the summary is missing, is for
     another workload, or was taken on a different kernel source."""
-    import hashlib
     try:
         text = open(TRAFFIC_SUMMARY).read()
         block = text.split("```json", 1)[1].split("```", 1)[0]
         data = json.loads(block)
-        sha = hashlib.sha256(open(NS_SOURCE, "rb").read()).hexdigest()
+        sha = ns_source_sha256()
     except (OSError, IndexError, ValueError):
         return None
-    if data.get("ns_gemm_hip_sha256") != sha or data.get("workload") != workload:
+    if data.get("ns_sources_sha256") != sha or data.get("workload") != workload:
         return None
     return data["fetch_bytes_per_launch"] + data["write_bytes_per_launch"]
 
@@ -52,14 +63,13 @@ def measured_mfma_util(workload):
     %) of each NS kernel from the committed counter summary, or None when
     it is missing, is for another workload, or was taken on a different
     kernel source."""
-    import hashlib
     try:
         text = open(MFMA_SUMMARY).read()
         data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-        sha = hashlib.sha256(open(NS_SOURCE, "rb").read()).hexdigest()
+        sha = ns_source_sha256()
     except (OSError, IndexError, ValueError):
         return None
-    if data.get("ns_gemm_hip_sha256") != sha or data.get("workload") != workload:
+    if data.get("ns_sources_sha256") != sha or data.get("workload") != workload:
         return None
     return {k: round(v["mfma_util_pct"], 1) for k, v in data["kernels"].items()}
 

@@ -117,7 +117,8 @@ void emit_super_tiles(int mat, int rows, int cols, bool tri, std::vector<Item>& 
     for (int C = tri ? (R / kSuperCols) * kSuperCols : 0; C < cols; C += kSuperCols)
       for (int a = R; a < std::min(rows, R + kSuperRows); ++a)
         for (int b = C; b < std::min(cols, C + kSuperCols); ++b)
-          if (!tri || a <= b) out.push_back(Item{mat, (a << 16) | b});
+          if (!tri || a <= b)
+            out.push_back(Item{mat, (static_cast<uint32_t>(a) << 16) | static_cast<uint32_t>(b)});
 }
 
 // Build every host-side table; no HIP call.
@@ -265,7 +266,8 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
       d.k1_count = static_cast<int32_t>((rp / muon::kEwTile) * (cp / muon::kEwTile));
       for (int64_t r = 0; r < rp / muon::kEwTile; ++r)
         for (int64_t c = 0; c < cp / muon::kEwTile; ++c)
-          p.k1_items.push_back(Item{m, static_cast<int32_t>((r << 16) | c)});
+          p.k1_items.push_back(
+              Item{m, (static_cast<uint32_t>(r) << 16) | static_cast<uint32_t>(c)});
     }
     w.k1_count = static_cast<int64_t>(p.k1_items.size()) - w.k1_begin;
     w.bytes = off;

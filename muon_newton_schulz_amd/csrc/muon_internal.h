@@ -51,9 +51,11 @@ struct MatDev {
 };
 
 // A tile work item: matrix index (plan-global) and packed tile coords.
+// Unsigned, so that a row tile of 32768 or more (a natural side of more
+// than 2^21 elements in 64-element tiles) decodes with a logical shift.
 struct Item {
   int32_t mat;
-  int32_t rc;  // (row_tile << 16) | col_tile
+  uint32_t rc;  // (row_tile << 16) | col_tile, each < 2^16
 };
 
 struct GemmArgs {

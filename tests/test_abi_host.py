@@ -210,3 +210,16 @@ def test_plan_flags_validate_before_any_hip_call():
     # the known flags pass validation and the call gets as far as the device
     for f in (0, 1, 2, 3):
         assert rc(f) not in (M.MUON_ERR_INVALID_ARG, M.MUON_ERR_BAD_SHAPE, M.MUON_ERR_BAD_DTYPE)
+
+
+def test_longest_side_a_plan_accepts():
+    # elementwise tile coordinates (64-element tiles of the side padded to
+    # the GEMM tile) are packed in 16 bits: bf16 NS pads to 256, so the
+    # longest side is 16383 * 256; fp32 NS pads to 64: 65535 * 64
+    ws = M.muon_workspace_size
+    for nsd, longest in (("bf16", 16383 * 256), ("fp32", 65535 * 64)):
+        for shape in ((1, longest), (longest, 1)):
+            assert ws([(0, *shape)], longest, nsd, nsd, nsd) > 0
+        for shape in ((1, longest + 1), (longest + 1, 1)):
+            assert _err(ws, [(0, *shape)], longest + 1, nsd, nsd, nsd) == M.MUON_ERR_BAD_SHAPE
+            assert "too large" in M.muon_last_error()
