@@ -149,6 +149,9 @@ typedef struct {
   int32_t split_diag_mats;    /* tiled bf16 matrices whose diagonal tiles of
                                  X X^T and A A compute only their upper blocks
                                  (below) */
+  int32_t fused_apply_mats;   /* matrices whose update can be applied by the
+                                 last phase 3 (muon_stage_ns_apply) */
+  int32_t reserved;
 } muon_plan_info_t;
 
 /* Host-only sizing: validates exactly as muon_plan_create and returns the
@@ -202,6 +205,8 @@ int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info);
  * Elements of the flat buffers not covered by a matrix are never touched.
  * With hp->clip set, every gradient is multiplied by clip->scale, and if
  * clip->skip is set params, momentum and out_update are left unchanged.
+ * Without out_update (and ns_steps >= 1) the last NS phase applies the
+ * update itself (muon_stage_ns_apply); the result is bitwise the same.
  * Concurrent steps on one workspace race; use one workspace per stream. */
 int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* momentum,
               void* workspace, size_t workspace_bytes, const muon_hparams_t* hp,
@@ -212,7 +217,9 @@ int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* m
  *   for it in [0, ns_steps): for phase in {1, 2 (only if ns_c != 0), 3}:
  *   muon_stage_ns_phase(w, it, phase); muon_stage_apply(w).
  * Phase 1: A = X X^T; phase 2: B = b A + c A A; phase 3: X <- a X + B X
- * (with c == 0, phase 3 uses b A for B). */
+ * (with c == 0, phase 3 uses b A for B).  The apply step is
+ * W <- (1 - lr wd) W - lr s O with s the update scale of scale_mode
+ * (optimizer tutorial 3.1, decoupled decay; K2 answer 3.1, 3.2). */
 int muon_stage_momentum(const muon_plan_t* plan, int32_t wave, const void* grads,
                         float* momentum, void* workspace, size_t workspace_bytes,
                         const muon_hparams_t* hp, hipStream_t stream);
@@ -222,6 +229,17 @@ int muon_stage_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
 int muon_stage_apply(const muon_plan_t* plan, int32_t wave, void* params, void* workspace,
                      size_t workspace_bytes, const muon_hparams_t* hp, float* out_update,
                      hipStream_t stream);
+/* muon_stage_ns_phase(w, ns_steps - 1, 3) followed by muon_stage_apply(w)
+ * with out_update NULL, bitwise, in fewer HBM passes: with bf16 NS and
+ * bf16 params in a 16-byte aligned buffer, every matrix whose offset and
+ * cols are multiples of 8 (muon_plan_info_t.fused_apply_mats) has its
+ * update applied by the phase-3 epilogue, which reads and writes W instead
+ * of writing X (X of the last iteration is then not in the workspace;
+ * muon_stage_export_x must not be asked for it); the others run the apply
+ * kernel.  ns_steps must be >= 1.  With hp->clip->skip set, params are
+ * left unchanged. */
+int muon_stage_ns_apply(const muon_plan_t* plan, int32_t wave, void* params, void* workspace,
+                        size_t workspace_bytes, const muon_hparams_t* hp, hipStream_t stream);
 
 /* Copy the current NS iterate of every matrix of a wave into a flat fp32
  * buffer at each matrix's elements, in the caller's [rows, cols] layout

@@ -34,6 +34,7 @@ EXPORTED = [
     "muon_workspace_size", "muon_plan_create", "muon_plan_create_ex", "muon_plan_destroy",
     "muon_plan_get_info",
     "muon_step", "muon_stage_momentum", "muon_stage_ns_phase", "muon_stage_apply",
+    "muon_stage_ns_apply",
     "muon_stage_export_x", "muon_stage_export_norms", "adamw_step", "adamw_step_ex",
     "muon_status_string",
     "muon_last_error", "grad_norm_clip_workspace_size", "grad_norm_clip",
@@ -99,7 +100,8 @@ class MuonPlanInfo(ctypes.Structure):
                 ("k1_tiles", ctypes.c_int64), ("syrk_tiles", ctypes.c_int64),
                 ("bx_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("ns_flops_per_iter_alg", ctypes.c_double), ("small_mats", ctypes.c_int32),
-                ("split_diag_mats", ctypes.c_int32)]
+                ("split_diag_mats", ctypes.c_int32), ("fused_apply_mats", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib_handle = None
@@ -129,6 +131,7 @@ def lib() -> ctypes.CDLL:
     L.muon_stage_momentum.argtypes = [P, I32, P, P, P, SZ, hp_p, P]
     L.muon_stage_ns_phase.argtypes = [P, I32, P, SZ, hp_p, I32, I32, P]
     L.muon_stage_apply.argtypes = [P, I32, P, P, SZ, hp_p, P, P]
+    L.muon_stage_ns_apply.argtypes = [P, I32, P, P, SZ, hp_p, P]
     L.muon_stage_export_x.argtypes = [P, I32, P, SZ, I32, P, P]
     L.muon_stage_export_norms.argtypes = [P, I32, P, SZ, P, P]
     L.adamw_step.argtypes = [P, I32, P, P, I32, P, P, I64, ctypes.POINTER(AdamWHParamsC), I64, P]
@@ -384,6 +387,18 @@ def muon_stage_apply(plan: MuonPlan, wave: int, params, workspace, hp, out_updat
     _check(lib().muon_stage_apply(ctypes.c_void_p(plan.handle), wave, _ptr(params),
                                   _ptr(workspace), _nbytes(workspace), ctypes.byref(h),
                                   _ptr(out_update), _stream(stream)))
+
+
+def muon_stage_ns_apply(plan: MuonPlan, wave: int, params, workspace, hp, stream=None,
+                        clip=None) -> None:
+    """Phase 3 of the last NS iteration with the update applied: bitwise
+    muon_stage_ns_phase(..., ns_steps - 1, 3) then muon_stage_apply(...)."""
+    _flat_args(plan, params=_buf(params, "params"))
+    _buf(workspace, "workspace")
+    h = _hp(hp, clip)
+    _check(lib().muon_stage_ns_apply(ctypes.c_void_p(plan.handle), wave, _ptr(params),
+                                     _ptr(workspace), _nbytes(workspace), ctypes.byref(h),
+                                     _stream(stream)))
 
 
 def muon_stage_export_x(plan: MuonPlan, wave: int, workspace, iter_done: int, out,

@@ -250,12 +250,6 @@ __global__ __launch_bounds__(256) void k_norm_finalize(const MatDev* __restrict_
   }
 }
 
-__device__ __forceinline__ float update_scale(int rows, int cols, int mode, float rms_target) {
-  if (mode == 0) return rms_target * sqrtf(static_cast<float>(rows > cols ? rows : cols));
-  if (mode == 1) return sqrtf(fmaxf(1.0f, static_cast<float>(rows) / static_cast<float>(cols)));
-  return 1.0f;
-}
-
 template <typename PT, typename UT>
 __global__ __launch_bounds__(256) void k_apply(const MatDev* __restrict__ mats,
                                                const Item* __restrict__ items,
@@ -272,8 +266,7 @@ __global__ __launch_bounds__(256) void k_apply(const MatDev* __restrict__ mats,
   const int r0 = (it.rc >> 16) * kEwTile, c0 = (it.rc & 0xffff) * kEwTile;
   const UT* X = ws + (x_final ? md.ws_x[1] : md.ws_x[0]);
   const float osc = use_inv ? inv[md.widx] : 1.0f;
-  const float decay = 1.0f - lr * wd;
-  const float step = lr * update_scale(md.rows, md.cols, scale_mode, rms_target);
+  const ApplyConsts ak = apply_consts(md.rows, md.cols, lr, wd, scale_mode, rms_target);
   if (vec4_ok(md, bufs_aligned)) {
     // thread = 4 consecutive columns x 4 rows (16 elements)
     const NatDims nd = nat_dims(md);
@@ -307,7 +300,10 @@ __global__ __launch_bounds__(256) void k_apply(const MatDev* __restrict__ mats,
         const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
         const f32x4v oo = o[q] * osc;
         const f32x4v w = V4<PT>::ld(params, e);
-        V4<PT>::st(params, e, decay * w - step * oo);
+        f32x4v wn;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wn[k] = apply_one(ak, w[k], oo[k]);
+        V4<PT>::st(params, e, wn);
         if (out_update) V4<float>::st(out_update, e, oo);
       }
     }
@@ -322,7 +318,7 @@ __global__ __launch_bounds__(256) void k_apply(const MatDev* __restrict__ mats,
       const int64_t e = md.off + static_cast<int64_t>(r) * md.cols + c;
       const float oo = o[q] * osc;
       const float w = Elem<PT>::ld(params, e);
-      Elem<PT>::st(params, e, decay * w - step * oo);
+      Elem<PT>::st(params, e, apply_one(ak, w, oo));
       if (out_update) out_update[e] = oo;
     }
   }

@@ -40,6 +40,8 @@ struct Wave {
   int64_t syrk_begin = 0, syrk_count = 0;  // phases 1 and 2 share the list
   int64_t bx_begin = 0, bx_count = 0;
   int64_t small_begin = 0, small_count = 0;  // into the small-matrix table
+  int64_t k7_begin = 0, k7_count = 0;  // elementwise tiles of the matrices whose
+                                       // update is not fused into phase 3
   size_t partial_off = 0, norm_off = 0, inv_off = 0;  // byte offsets in the workspace
   size_t bytes = 0;
 };
@@ -58,7 +60,7 @@ struct muon_plan {
   int tile = 0;
   size_t ws_bytes = 0;
   std::vector<MatDev> mats;
-  std::vector<Item> k1_items, syrk_items, bx_items;
+  std::vector<Item> k1_items, syrk_items, bx_items, k7_items;
   std::vector<int32_t> small_list;  // matrices run by the fused small-matrix kernel
   std::vector<Wave> waves;
   // device copies
@@ -67,6 +69,7 @@ struct muon_plan {
   Item* d_k1 = nullptr;
   Item* d_syrk = nullptr;
   Item* d_bx = nullptr;
+  Item* d_k7 = nullptr;
   int32_t* d_small = nullptr;
   double flops_per_iter = 0.0;
 };
@@ -193,6 +196,12 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
               d.m_pad / T <= muon::kDiagMaxTiles)
                  ? 1
                  : 0;
+    // the fused update writes 16-byte pieces of 8 parameters along a
+    // natural row
+    d.fuse = (ns_dtype == MUON_DTYPE_BF16 && param_dtype == MUON_DTYPE_BF16 && !d.small &&
+              d.off % 8 == 0 && d.cols % 8 == 0)
+                 ? 1
+                 : 0;
     const double m = std::min(d.rows, d.cols), n = std::max(d.rows, d.cols);
     p.flops_per_iter += m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n;
   }
@@ -270,6 +279,10 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
               Item{m, (static_cast<uint32_t>(r) << 16) | static_cast<uint32_t>(c)});
     }
     w.k1_count = static_cast<int64_t>(p.k1_items.size()) - w.k1_begin;
+    w.k7_begin = static_cast<int64_t>(p.k7_items.size());
+    for (int64_t k = w.k1_begin; k < w.k1_begin + w.k1_count; ++k)
+      if (!p.mats[p.k1_items[k].mat].fuse) p.k7_items.push_back(p.k1_items[k]);
+    w.k7_count = static_cast<int64_t>(p.k7_items.size()) - w.k7_begin;
     w.bytes = off;
     ws_max = std::max(ws_max, off);
 
@@ -319,7 +332,8 @@ int upload_plan(muon_plan& p) {
   const size_t b_syrk = align_up(p.syrk_items.size() * sizeof(Item), kAlign);
   const size_t b_bx = align_up(p.bx_items.size() * sizeof(Item), kAlign);
   const size_t b_small = align_up(p.small_list.size() * sizeof(int32_t), kAlign);
-  const size_t total = b_mats + b_k1 + b_syrk + b_bx + b_small;
+  const size_t b_k7 = align_up(p.k7_items.size() * sizeof(Item), kAlign);
+  const size_t total = b_mats + b_k1 + b_syrk + b_bx + b_small + b_k7;
   if (total == 0) return MUON_OK;
   e = hipMalloc(&p.d_tables, total);
   if (e != hipSuccess) return hip_fail(e, "hipMalloc(plan tables)");
@@ -329,6 +343,7 @@ int upload_plan(muon_plan& p) {
   p.d_syrk = reinterpret_cast<Item*>(base + b_mats + b_k1);
   p.d_bx = reinterpret_cast<Item*>(base + b_mats + b_k1 + b_syrk);
   p.d_small = reinterpret_cast<int32_t*>(base + b_mats + b_k1 + b_syrk + b_bx);
+  p.d_k7 = reinterpret_cast<Item*>(base + b_mats + b_k1 + b_syrk + b_bx + b_small);
   std::vector<char> host(total, 0);
   std::memcpy(host.data(), p.mats.data(), p.mats.size() * sizeof(MatDev));
   std::memcpy(host.data() + b_mats, p.k1_items.data(), p.k1_items.size() * sizeof(Item));
@@ -337,6 +352,8 @@ int upload_plan(muon_plan& p) {
               p.bx_items.size() * sizeof(Item));
   std::memcpy(host.data() + b_mats + b_k1 + b_syrk + b_bx, p.small_list.data(),
               p.small_list.size() * sizeof(int32_t));
+  std::memcpy(host.data() + b_mats + b_k1 + b_syrk + b_bx + b_small, p.k7_items.data(),
+              p.k7_items.size() * sizeof(Item));
   e = hipMemcpy(p.d_tables, host.data(), total, hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy(plan tables)");
   return MUON_OK;
@@ -409,6 +426,12 @@ muon::GemmArgs gemm_args(const muon_plan_t* p, const Wave& w, void* ws, const mu
   g.e2_diag = hp->ns_a;
   g.first = iter == 0;
   g.x_cur = iter & 1;
+  g.params = nullptr;
+  g.clip = nullptr;
+  g.lr = hp->lr;
+  g.wd = hp->weight_decay;
+  g.rms_target = hp->rms_target;
+  g.scale_mode = hp->scale_mode;
   return g;
 }
 
@@ -499,7 +522,12 @@ int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {
   info->ns_flops_per_iter_alg = plan->flops_per_iter;
   info->small_mats = static_cast<int32_t>(plan->small_list.size());
   info->split_diag_mats = 0;
-  for (const muon::MatDev& d : plan->mats) info->split_diag_mats += d.diag;
+  info->fused_apply_mats = 0;
+  for (const muon::MatDev& d : plan->mats) {
+    info->split_diag_mats += d.diag;
+    info->fused_apply_mats += d.fuse;
+  }
+  info->reserved = 0;
   return MUON_OK;
 }
 
@@ -530,15 +558,21 @@ namespace {
 
 // Phase `phase` of NS iteration `iter` for the wave's tiled matrices; with
 // small_iters > 0 (phase 3 only) also small_iters whole iterations of its
-// small matrices, starting at `iter`.
+// small matrices, starting at `iter`.  fused_params (phase 3 of the last
+// iteration, bf16 engine): apply the update of the matrices with
+// MatDev::fuse in the epilogue.
 int run_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
                  const muon_hparams_t* hp, int32_t iter, int32_t phase, int32_t small_iters,
-                 hipStream_t stream) {
+                 hipStream_t stream, void* fused_params = nullptr) {
   const Wave& w = plan->waves[wave];
   const Item* items = phase == 3 ? plan->d_bx + w.bx_begin : plan->d_syrk + w.syrk_begin;
   const int n = static_cast<int>(phase == 3 ? w.bx_count : w.syrk_count);
   muon::GemmArgs g = gemm_args(plan, w, workspace, hp, iter, items);
   g.n_items = n;
+  if (fused_params != nullptr) {
+    g.params = static_cast<uint16_t*>(fused_params);
+    g.clip = clip_of(hp->clip);
+  }
   hipError_t e = muon::launch_ns_phase(plan->ns_dtype, phase, n, plan->n_cu, g, stream);
   if (e != hipSuccess) return hip_fail(e, "NS kernel launch");
   if (small_iters > 0 && w.small_count > 0) {
@@ -565,6 +599,44 @@ int muon_stage_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
   return run_ns_phase(plan, wave, workspace, hp, iter, phase, phase == 3 ? 1 : 0, stream);
 }
 
+namespace {
+
+// The apply kernel over `count` elementwise tiles of the wave.
+int run_apply(const muon_plan_t* plan, const Wave& w, const Item* items, int64_t count,
+              void* params, void* workspace, const muon_hparams_t* hp, float* out_update,
+              hipStream_t stream) {
+  const hipError_t e = muon::launch_apply(
+      plan->d_mats, items, static_cast<int>(count), plan->param_dtype, plan->ns_dtype, params,
+      workspace, reinterpret_cast<const float*>(ws_bytes_ptr(workspace, w.inv_off)),
+      hp->ns_steps == 0 ? 1.0f : 0.0f, hp->ns_steps & 1, hp->lr, hp->weight_decay,
+      hp->scale_mode, hp->rms_target, out_update, clip_of(hp->clip), stream);
+  if (e != hipSuccess) return hip_fail(e, "apply kernel launch");
+  return MUON_OK;
+}
+
+// Phase 3 of the last iteration and the update: fused into phase 3's
+// epilogue for the matrices that allow it (bf16 engine and parameters, a
+// 16-byte aligned parameter buffer), the apply kernel for the others.
+int run_ns_apply(const muon_plan_t* plan, int32_t wave, void* params, void* workspace,
+                 const muon_hparams_t* hp, int32_t small_iters, hipStream_t stream) {
+  const Wave& w = plan->waves[wave];
+  const int32_t last = hp->ns_steps - 1;
+  const bool fused = plan->ns_dtype == MUON_DTYPE_BF16 &&
+                     plan->param_dtype == MUON_DTYPE_BF16 &&
+                     reinterpret_cast<uintptr_t>(params) % 16 == 0;
+  int rc = run_ns_phase(plan, wave, workspace, hp, last, 3, small_iters, stream,
+                        fused ? params : nullptr);
+  if (rc != MUON_OK) return rc;
+  if (!fused)
+    return run_apply(plan, w, plan->d_k1 + w.k1_begin, w.k1_count, params, workspace, hp,
+                     nullptr, stream);
+  if (w.k7_count == 0) return MUON_OK;
+  return run_apply(plan, w, plan->d_k7 + w.k7_begin, w.k7_count, params, workspace, hp,
+                   nullptr, stream);
+}
+
+}  // namespace
+
 int muon_stage_apply(const muon_plan_t* plan, int32_t wave, void* params, void* workspace,
                      size_t workspace_bytes, const muon_hparams_t* hp, float* out_update,
                      hipStream_t stream) {
@@ -573,14 +645,19 @@ int muon_stage_apply(const muon_plan_t* plan, int32_t wave, void* params, void* 
   if ((rc = check_hparams(hp)) != MUON_OK) return rc;
   if (params == nullptr) return fail(MUON_ERR_INVALID_ARG, "params is null");
   const Wave& w = plan->waves[wave];
-  const hipError_t e = muon::launch_apply(
-      plan->d_mats, plan->d_k1 + w.k1_begin, static_cast<int>(w.k1_count), plan->param_dtype,
-      plan->ns_dtype, params, workspace,
-      reinterpret_cast<const float*>(ws_bytes_ptr(workspace, w.inv_off)),
-      hp->ns_steps == 0 ? 1.0f : 0.0f, hp->ns_steps & 1, hp->lr, hp->weight_decay,
-      hp->scale_mode, hp->rms_target, out_update, clip_of(hp->clip), stream);
-  if (e != hipSuccess) return hip_fail(e, "apply kernel launch");
-  return MUON_OK;
+  return run_apply(plan, w, plan->d_k1 + w.k1_begin, w.k1_count, params, workspace, hp,
+                   out_update, stream);
+}
+
+int muon_stage_ns_apply(const muon_plan_t* plan, int32_t wave, void* params, void* workspace,
+                        size_t workspace_bytes, const muon_hparams_t* hp, hipStream_t stream) {
+  int rc = check_step_common(plan, wave, workspace, workspace_bytes);
+  if (rc != MUON_OK) return rc;
+  if ((rc = check_hparams(hp)) != MUON_OK) return rc;
+  if (params == nullptr) return fail(MUON_ERR_INVALID_ARG, "params is null");
+  if (hp->ns_steps < 1) return fail(MUON_ERR_INVALID_ARG, "ns_steps must be >= 1");
+  // like muon_stage_ns_phase, the small matrices run one iteration
+  return run_ns_apply(plan, wave, params, workspace, hp, 1, stream);
 }
 
 int muon_stage_export_x(const muon_plan_t* plan, int32_t wave, const void* workspace,
@@ -625,17 +702,26 @@ int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* m
     rc = muon_stage_momentum(plan, w, grads, momentum, workspace, workspace_bytes, hp, stream);
     if (rc != MUON_OK) return rc;
     // tiled matrices phase by phase; the small matrices run all their
-    // iterations in one launch (bitwise the same as one per iteration)
+    // iterations in one launch (bitwise the same as one per iteration).
+    // Without out_update, the last phase 3 applies the update itself.
+    const bool fuse = out_update == nullptr && hp->ns_steps >= 1;
     for (int32_t it = 0; it < hp->ns_steps; ++it) {
+      const int32_t small_iters = it == 0 ? hp->ns_steps : 0;
       rc = run_ns_phase(plan, w, workspace, hp, it, 1, 0, stream);
       if (rc == MUON_OK && hp->ns_c != 0.0f)
         rc = run_ns_phase(plan, w, workspace, hp, it, 2, 0, stream);
-      if (rc == MUON_OK)
-        rc = run_ns_phase(plan, w, workspace, hp, it, 3, it == 0 ? hp->ns_steps : 0, stream);
+      if (rc == MUON_OK) {
+        if (fuse && it == hp->ns_steps - 1)
+          rc = run_ns_apply(plan, w, params, workspace, hp, small_iters, stream);
+        else
+          rc = run_ns_phase(plan, w, workspace, hp, it, 3, small_iters, stream);
+      }
       if (rc != MUON_OK) return rc;
     }
-    rc = muon_stage_apply(plan, w, params, workspace, workspace_bytes, hp, out_update, stream);
-    if (rc != MUON_OK) return rc;
+    if (!fuse) {
+      rc = muon_stage_apply(plan, w, params, workspace, workspace_bytes, hp, out_update, stream);
+      if (rc != MUON_OK) return rc;
+    }
   }
   return MUON_OK;
 }

@@ -44,6 +44,10 @@ struct MatDev {
   int32_t small;         // 1: NS runs in the fused one-workgroup kernel
   int32_t diag;          // 1: diagonal tiles of the symmetric products
                          // compute only their upper blocks
+  int32_t fuse;          // 1: the last phase 3 can apply the update to W in
+                         // its epilogue (tiled bf16 NS, bf16 params, offset
+                         // and cols multiples of 8)
+  int32_t reserved;
   // element offsets (in NS elements) into the workspace
   int64_t ws_x[2];       // X : m_pad x n_pad, ping-pong
   int64_t ws_a;          // A : m_pad x m_pad
@@ -56,6 +60,15 @@ struct MatDev {
 struct Item {
   int32_t mat;
   uint32_t rc;  // (row_tile << 16) | col_tile, each < 2^16
+};
+
+// Device view of muon_clip_state_t (same layout): the gradient scale and
+// the skip flag of a guarded step.  A null pointer means scale 1, no skip.
+struct ClipState {
+  float norm;
+  float scale;
+  int32_t skip;
+  int32_t reserved;
 };
 
 struct GemmArgs {
@@ -71,15 +84,14 @@ struct GemmArgs {
   int32_t first;      // first NS iteration: fold the normalisation in
   int32_t x_cur;      // X buffer read by phases 1 and 3 (phase 3 writes 1 - x_cur)
   int32_t n_items;    // tile-list length (the persistent grid walks it)
-};
-
-// Device view of muon_clip_state_t (same layout): the gradient scale and
-// the skip flag of a guarded step.  A null pointer means scale 1, no skip.
-struct ClipState {
-  float norm;
-  float scale;
-  int32_t skip;
-  int32_t reserved;
+  // Phase 3 of the last iteration with the update applied in the epilogue
+  // (bf16 engine): for matrices with MatDev::fuse, W <- decay W - step O
+  // with O the bf16 value X' would hold; X' is not written for them.
+  // params == nullptr: plain phase 3.
+  uint16_t* params;   // flat bf16 parameters
+  const ClipState* clip;  // guarded step (skip: W untouched), or null
+  float lr, wd, rms_target;
+  int32_t scale_mode;
 };
 
 // kernel launchers (defined in the .hip files)
@@ -124,6 +136,26 @@ hipError_t launch_state_stats(const float* x, int64_t n, void* partials, void* o
 // muon_last_error() on the calling thread and return the status code.
 int set_error(int code, const std::string& msg);
 int set_hip_error(hipError_t e, const char* what);
+
+// The update of one parameter, shared by the apply kernel and the fused
+// phase-3 epilogue so that both give the same bits: with
+// decay = 1 - lr*wd and step = lr * s (s the matrix's update scale),
+// W' = decay*W - step*O, written with explicit fmas.
+__device__ __forceinline__ float update_scale(int rows, int cols, int mode, float rms_target) {
+  if (mode == 0) return rms_target * sqrtf(static_cast<float>(rows > cols ? rows : cols));
+  if (mode == 1) return sqrtf(fmaxf(1.0f, static_cast<float>(rows) / static_cast<float>(cols)));
+  return 1.0f;
+}
+struct ApplyConsts {
+  float decay, step;
+};
+__device__ __forceinline__ ApplyConsts apply_consts(int rows, int cols, float lr, float wd,
+                                                    int mode, float rms_target) {
+  return ApplyConsts{fmaf(-lr, wd, 1.0f), lr * update_scale(rows, cols, mode, rms_target)};
+}
+__device__ __forceinline__ float apply_one(const ApplyConsts& k, float w, float o) {
+  return fmaf(-k.step, o, k.decay * w);
+}
 
 // bf16 <-> fp32 (bf16 stored as its 16-bit pattern)
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

@@ -170,6 +170,16 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Fused update of 8 bf16 parameters: W' = decay W - step O, O the 8 bf16
+// values phase 3 would store (the apply kernel's arithmetic, same bits).
+__device__ __forceinline__ u32x4_t apply8(const ApplyConsts& k, u32x4_t w, u32x4_t o) {
+  u32x4_t r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    r[e] = pack2(apply_one(k, lo_bf(w[e]), lo_bf(o[e])), apply_one(k, hi_bf(w[e]), hi_bf(o[e])));
+  return r;
+}
+
 // The lane id, hidden from the optimiser (see the epilogue).
 __device__ __forceinline__ int opaque_lane(int lane) {
   asm volatile("" : "+v"(lane));
@@ -196,7 +206,9 @@ __device__ __forceinline__ int tile_role(int phase, int ti, int tj, int wave) {
 }
 
 // One 256x256 output tile: operand pipeline, MFMA main loop, epilogue.
-template <int PHASE, int ROLE>
+// APPLY (phase 3 only): a matrix with MatDev::fuse gets the update applied
+// to its parameters instead of X' written.
+template <int PHASE, int ROLE, bool APPLY = false>
 __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, const int ti,
                                         const int tj, const float inv, uint16_t* smem) {
   // MFMA m = 4 bj + bi runs iff bit m is set
@@ -404,6 +416,24 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // loads: row lane/16 + 4u, 16-byte chunk lane%16).
   const int i0w = ti * BT + wie * 128, j0w = tj * BT + wje * 128 + qshift;
   constexpr bool aterm = PHASE == 2;
+  // Fused update (phase 3 of the last iteration): W instead of X' for this
+  // matrix.  A natural row of W is a row of the tile (wide matrix) or a
+  // column of it (tall matrix).  A wide matrix's W sub-tile is loaded like
+  // phase 2's A, while the last stage computes, and updated in the staging
+  // layout; a tall one is updated after the staging, through the
+  // transposed pass.
+  bool to_w = false;
+  ApplyConsts ak{0.0f, 0.0f};
+  uint16_t* Wm = nullptr;
+  if constexpr (APPLY) {
+    if (md.fuse) {
+      if (g.clip != nullptr && g.clip->skip) return;  // guarded step: W untouched
+      to_w = true;
+      ak = apply_consts(md.rows, md.cols, g.lr, g.wd, g.scale_mode, g.rms_target);
+      Wm = g.params + md.off;
+    }
+  }
+  const bool w_rows = APPLY && to_w && !md.trans;
   u32x4_t apre[32];
   if constexpr (aterm) {
     const int pl = opaque_lane(lane);
@@ -412,6 +442,20 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 #pragma unroll
     for (int u = 0; u < 32; ++u)
       apre[u] = *reinterpret_cast<const u32x4_t*>(Ao + static_cast<int64_t>(4 * u) * md.m_pad);
+  }
+  if constexpr (APPLY) {
+    if (w_rows) {
+      // row i0w + lane/16 + 4u, 8 columns from j0w + 8*(lane%16); a piece
+      // past W's rows or cols is not loaded (cols is a multiple of 8)
+      const int pl = opaque_lane(lane);
+      const int wc = j0w + 8 * (pl & 15);
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int wr = i0w + (pl >> 4) + 4 * u;
+        if (wr < md.rows && wc < md.cols)
+          apre[u] = *reinterpret_cast<const u32x4_t*>(Wm + static_cast<int64_t>(wr) * md.cols + wc);
+      }
+    }
   }
   stage(kt, F_{}, F_{});
   __syncthreads();
@@ -457,8 +501,27 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     return r * 128 + (((2 * rc) ^ (gr | (u & 6))) << 2);
   };
 
-  if constexpr (aterm) {
-    // b*A term: the prefetched A sub-tile into the staging layout
+  // Fused update: this lane's 32 pieces of 8 parameters.  A wide matrix's
+  // piece u is W[i][j..j+7] with i = i0w + lane/16 + 4u, j = j0w + 8*(lane%16)
+  // (the row stores' chunks); a tall matrix's is W[j][i..i+7] with
+  // j = j0w + 32*(u%4) + 16*((lane/16)%2) + lane%16, i = i0w + 16*(u/4) +
+  // 8*(lane/32) (the transposed pass's pieces).  cols is a multiple of 8, so
+  // a piece is inside W or outside it whole.
+  auto w_piece = [&](int u, int64_t& e) {
+    int wr, wc;
+    if (!md.trans) {
+      wr = i0w + (elane >> 4) + 4 * u;
+      wc = j0w + 8 * rc;
+    } else {
+      wr = j0w + 32 * (u & 3) + 16 * ((elane >> 4) & 1) + (elane & 15);
+      wc = i0w + 16 * (u >> 2) + 8 * (elane >> 5);
+    }
+    e = static_cast<int64_t>(wr) * md.cols + wc;
+    return wr < md.rows && wc < md.cols;
+  };
+  if (aterm || w_rows) {
+    // b*A term, or the fused update of a wide matrix: the prefetched A or
+    // W sub-tile into the staging layout
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
       u32x4_t v = apre[u];
@@ -498,10 +561,73 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] += efrow == 8 * q + 4 * hl + e ? dval : 0.0f;
         }
-        *slotp = u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])};
+        if (APPLY && w_rows) {
+          // O rounded to bf16 as X' would hold it, then W' = decay W - step O
+          const u32x2_t w0 = *slotp;
+          const uint32_t o0 = pack2(v[0], v[1]), o1 = pack2(v[2], v[3]);
+          *slotp = u32x2_t{pack2(apply_one(ak, lo_bf(w0[0]), lo_bf(o0)),
+                                 apply_one(ak, hi_bf(w0[0]), hi_bf(o0))),
+                           pack2(apply_one(ak, lo_bf(w0[1]), lo_bf(o1)),
+                                 apply_one(ak, hi_bf(w0[1]), hi_bf(o1)))};
+        } else {
+          *slotp = u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])};
+        }
       }
     }
   __syncthreads();
+
+  if constexpr (APPLY) {
+    if (to_w) {
+      if (!md.trans) {
+        // the staged tile holds W': row stores into W
+#pragma unroll 8
+        for (int u = 0; u < 32; ++u) {
+          int64_t e;
+          if (!w_piece(u, e)) continue;
+          u32x4_t v = *reinterpret_cast<const u32x4_t*>(S + row_slot16(u));
+          if (u & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
+          *reinterpret_cast<u32x4_t*>(Wm + e) = v;
+        }
+      } else {
+        // All 32 loads are issued first (the accumulators are staged and
+        // their registers free), so one memory latency covers them: a wait
+        // for loads would also wait for every store issued before it.
+        u32x4_t wv[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          int64_t e;
+          if (w_piece(u, e)) wv[u] = *reinterpret_cast<const u32x4_t*>(Wm + e);
+        }
+        // W' = decay W - step O for the 32 pieces, O read back transposed
+        const int s = elane & 15, G = elane >> 4;
+        const uint32_t sbase = lds_addr(S);
+        static_for<0, 4>([&](auto b_c) {
+          constexpr int u0 = 8 * decltype(b_c)::value;
+          s16x4_t tr[16];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            const int u = u0 + v;
+            const int jb = (u & 3) * 32, ib = (u >> 2) * 16;
+            const int ir = ib + 8 * (G >> 1) + (s >> 2);
+            const int jc = jb + 16 * (G & 1) + 4 * (s & 3);
+            tr[2 * v] = ld_tr_async<0>(sbase + 2 * stg(ir, jc));
+            tr[2 * v + 1] = ld_tr_async<0>(sbase + 2 * stg(ir + 4, jc));
+          }
+          wait_lds16(tr);
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            int64_t e;
+            if (!w_piece(u0 + v, e)) continue;
+            const u32x4_t o = __builtin_bit_cast(
+                u32x4_t,
+                __builtin_shufflevector(tr[2 * v], tr[2 * v + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            *reinterpret_cast<u32x4_t*>(Wm + e) = apply8(ak, wv[u0 + v], o);
+          }
+        });
+      }
+      return;
+    }
+  }
 
   // row stores: 16 bytes per lane, 4 rows of 256 bytes per instruction;
   // ROLE 1 stores its upper blocks (block row r/32 <= block column rc/4),
@@ -586,6 +712,24 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g, const Item* __re
     if (PHASE != 3 && role == 1) ns_tile<PHASE, 1>(g, md, ti, tj, inv, smem);
     else if (PHASE != 3 && role == 2) ns_tile<PHASE, 2>(g, md, ti, tj, inv, smem);
     else ns_tile<PHASE, 0>(g, md, ti, tj, inv, smem);
+  }
+}
+
+// Phase 3 of the last iteration with the update applied in the epilogue
+// (GemmArgs::params): the same tile walk as k_ns_bf16<3>.
+__global__ __launch_bounds__(256, 1) void k_ns_bf16_apply(GemmArgs g, const Item* __restrict__ items,
+                                                          const MatDev* __restrict__ mats,
+                                                          const float* __restrict__ invs) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * 2 * BT * BK];  // 128 KiB
+  bool busy = false;
+  for (int idx = blockIdx.x; idx < g.n_items; idx += gridDim.x) {
+    const Item it = items[idx];
+    if (it.mat < 0) continue;  // padding of the XCD-grouped order
+    const MatDev md = mats[it.mat];
+    const float inv = g.first ? invs[md.widx] : 1.0f;
+    if (busy) __syncthreads();  // the previous tile's epilogue is done with LDS
+    busy = true;
+    ns_tile<3, 0, true>(g, md, it.rc >> 16, it.rc & 0xffff, inv, smem);
   }
 }
 
@@ -697,7 +841,10 @@ hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
   const dim3 block(256);
   if (ns_dtype == 1) {
     const dim3 grid(n_items < n_cu ? n_items : n_cu);
-    if (phase == 1)
+    if (phase == 3 && args.params != nullptr)
+      hipLaunchKernelGGL(k_ns_bf16_apply, grid, block, 0, s, args, args.items, args.mats,
+                         args.inv);
+    else if (phase == 1)
       hipLaunchKernelGGL(k_ns_bf16<1>, grid, block, 0, s, args, args.items, args.mats, args.inv);
     else if (phase == 2)
       hipLaunchKernelGGL(k_ns_bf16<2>, grid, block, 0, s, args, args.items, args.mats, args.inv);

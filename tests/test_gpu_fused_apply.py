@@ -1,0 +1,161 @@
+"""The update applied by the last NS phase (muon_stage_ns_apply, and
+muon_step without out_update) against the separate apply kernel (muon_step
+with out_update, muon_stage_apply): params and momentum must be bitwise
+equal.  Both compute W' = fma(-step, O, decay * W) from the same bf16 O, so
+the fused path needs no tolerance of its own; the unfused path is checked
+against the oracle in test_gpu_parity.py.
+
+Matrices are fused when the NS and the params are bf16, the parameter
+buffer is 16-byte aligned and the matrix's offset and cols are multiples of
+8 (wide ones write W rows from the tile rows, tall ones through the
+transposed pass); the others, and the small matrices, keep the apply kernel.
+"""
+
+import pytest
+import torch
+
+import muon_newton_schulz_amd as M
+from muon_newton_schulz_amd import workloads as W
+
+from test_gpu_parity import CUBIC, QUINTIC, mhp
+
+pytestmark = pytest.mark.gpu
+
+BF16 = torch.bfloat16
+
+# (rows, cols, fused if the offset is a multiple of 8)
+SHAPES = [
+    (256, 512, True),     # wide, on the grid
+    (520, 296, True),     # tall (transposed pass), cols % 8 == 0
+    (520, 300, False),    # tall, cols % 8 == 4
+    (700, 1000, True),    # wide, rows off the tile grid
+    (1000, 776, True),    # tall, rows off the grid
+    (1000, 700, False),   # tall, cols % 8 == 4
+    (129, 8, False),      # small-matrix path
+    (64, 64, False),      # small-matrix path
+    (2048, 5632, True),
+    (5632, 2048, True),
+    (300, 520, True),     # offset made odd below: not fused
+]
+
+
+def _layout(shapes, misalign=(10,)):
+    mats, o, fused = [], 16, 0
+    for k, (r, c, f) in enumerate(shapes):
+        if k in misalign:
+            o += 3                         # an offset that is not a multiple of 8
+        mats.append((o, r, c))
+        fused += int(f and o % 8 == 0)
+        o += r * c
+        o = (o + 7) // 8 * 8 + 8           # next offset aligned (gaps stay untouched)
+    return mats, o + 8, fused
+
+
+class Case:
+    def __init__(self, gpu, mats, n, seed, pdt="bf16"):
+        g = torch.Generator(device=gpu)
+        g.manual_seed(seed)
+        dt = W.TORCH_DTYPE[pdt]
+        self.params = (torch.randn(n, generator=g, device=gpu) * 0.02).to(dt)
+        self.grads = (torch.randn(n, generator=g, device=gpu) * 0.02).to(BF16)
+        self.mom = torch.zeros(n, device=gpu)
+        self.plan = M.muon_plan_create(mats, n, pdt, "bf16", "bf16")
+        self.ws = self.plan.alloc_workspace(gpu)
+        self.out = torch.zeros(n, device=gpu)
+
+
+@pytest.mark.parametrize("coef", [QUINTIC, CUBIC])
+def test_fused_step_is_bitwise_the_apply_kernel(gpu, coef):
+    mats, n, n_fused = _layout(SHAPES)
+    a = Case(gpu, mats, n, 5)
+    b = Case(gpu, mats, n, 5)
+    assert a.plan.info().fused_apply_mats == n_fused == 6
+    hp = mhp(coef)
+    p0 = a.params.clone()
+    for _ in range(2):  # the second step starts from a nonzero momentum
+        M.muon_step(a.plan, a.params, a.grads, a.mom, a.ws, hp)            # fused
+        M.muon_step(b.plan, b.params, b.grads, b.mom, b.ws, hp, b.out)     # apply kernel
+    torch.cuda.synchronize()
+    assert torch.equal(a.params.view(torch.int16), b.params.view(torch.int16))
+    assert torch.equal(a.mom, b.mom)
+    assert not torch.equal(a.params, p0)
+
+
+def test_stage_ns_apply_composes_like_the_step(gpu):
+    mats, n, _ = _layout(SHAPES)
+    a = Case(gpu, mats, n, 6)
+    b = Case(gpu, mats, n, 6)
+    hp = mhp(QUINTIC)
+    M.muon_stage_momentum(a.plan, 0, a.grads, a.mom, a.ws, hp)
+    for it in range(hp.ns_steps):
+        for ph in (1, 2):
+            M.muon_stage_ns_phase(a.plan, 0, a.ws, hp, it, ph)
+        if it < hp.ns_steps - 1:
+            M.muon_stage_ns_phase(a.plan, 0, a.ws, hp, it, 3)
+    M.muon_stage_ns_apply(a.plan, 0, a.params, a.ws, hp)
+    M.muon_step(b.plan, b.params, b.grads, b.mom, b.ws, hp, b.out)
+    torch.cuda.synchronize()
+    assert torch.equal(a.params.view(torch.int16), b.params.view(torch.int16))
+    assert torch.equal(a.mom, b.mom)
+
+
+def test_fused_step_over_waves_and_fallbacks(gpu):
+    mats, n, _ = _layout(SHAPES)
+    hp = mhp(QUINTIC, steps=3, scale_mode=1)
+    # waves: a workspace cap that splits the matrices
+    a = Case(gpu, mats, n, 7)
+    cap = a.plan.workspace_bytes * 6 // 10   # one of the two large matrices per wave
+    capped = M.muon_plan_create(mats, n, "bf16", "bf16", "bf16", cap)
+    assert capped.info().n_waves > 1
+    ws = capped.alloc_workspace(gpu)
+    b = Case(gpu, mats, n, 7)
+    M.muon_step(capped, a.params, a.grads, a.mom, ws, hp)
+    M.muon_step(b.plan, b.params, b.grads, b.mom, b.ws, hp, b.out)
+    torch.cuda.synchronize()
+    assert torch.equal(a.params.view(torch.int16), b.params.view(torch.int16))
+    # a parameter buffer 2 bytes off 16-byte alignment: the apply kernel runs
+    base = torch.zeros(n + 1, dtype=BF16, device=gpu)
+    c = Case(gpu, mats, n, 8)
+    base[1:].copy_(c.params)
+    d = Case(gpu, mats, n, 8)
+    M.muon_step(c.plan, base[1:], c.grads, c.mom, c.ws, hp)
+    M.muon_step(d.plan, d.params, d.grads, d.mom, d.ws, hp, d.out)
+    torch.cuda.synchronize()
+    assert torch.equal(base[1:].view(torch.int16), d.params.view(torch.int16))
+    assert base[0].item() == 0.0
+    # fp32 params: never fused
+    e = Case(gpu, mats, n, 9, pdt="fp32")
+    assert e.plan.info().fused_apply_mats == 0
+
+
+def test_guard_skip_leaves_params_alone(gpu):
+    mats, n, _ = _layout(SHAPES)
+    a = Case(gpu, mats, n, 10)
+    clip = torch.zeros(4, dtype=torch.int32, device=gpu)
+    clip.view(torch.float32)[1] = 1.0   # scale
+    clip[2] = 1                          # skip
+    p0, m0 = a.params.clone(), a.mom.clone()
+    M.muon_step(a.plan, a.params, a.grads, a.mom, a.ws, mhp(QUINTIC), clip=clip)
+    torch.cuda.synchronize()
+    assert torch.equal(a.params.view(torch.int16), p0.view(torch.int16))
+    assert torch.equal(a.mom, m0)
+
+
+def test_dense_stack_fused_full_size(gpu):
+    """The dense d2048 x 16 stack as timed: every matrix fused, W bitwise
+    the apply kernel's."""
+    wl = W.workload("dense_d2048_l16")
+    hp = mhp(QUINTIC)
+    res = []
+    for with_out in (False, True):
+        inp = W.make_muon_inputs(wl, gpu, step=1)
+        plan = M.muon_plan_create(wl.mats(), wl.muon_numel(), "bf16", "bf16", "bf16")
+        assert plan.info().fused_apply_mats == 112
+        ws = plan.alloc_workspace(gpu)
+        out = torch.zeros(wl.muon_numel(), device=gpu) if with_out else None
+        M.muon_step(plan, inp.params, inp.grads, inp.momentum, ws, hp, out)
+        torch.cuda.synchronize()
+        res.append(inp.params.view(torch.int16).clone())
+        del inp, ws, out
+        torch.cuda.empty_cache()
+    assert torch.equal(res[0], res[1])
