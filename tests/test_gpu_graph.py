@@ -1,7 +1,8 @@
 """The optimizer step captured in a HIP graph: the library's steps enqueue
 kernels only (no allocation, no memset, no host synchronisation), so a
 caller can capture one whole step -- gradient-norm clip, Muon over small
-(fused) and tiled matrices, AdamW -- and replay it.  Every replay must be
+(fused) and tiled matrices, with the update applied by its own kernel or by
+the last NS phase, AdamW -- and replay it.  Every replay must be
 bitwise the eager step from the same state; eager work and host
 synchronisation run between the replays.  AdamW's step count and every
 hyper-parameter are fixed at capture, so the eager reference uses the same
@@ -20,10 +21,12 @@ pytestmark = pytest.mark.gpu
 
 class State:
     def __init__(self, gpu, seed):
-        mats, o = [], 3
-        for r, c in [(128, 256), (96, 200), (300, 520), (520, 300), (64, 64)]:
+        # offsets on 8-element boundaries: (300, 520) and (520, 296) can take
+        # the fused update, (520, 300) cannot (cols % 8 != 0)
+        mats, o = [], 8
+        for r, c in [(128, 256), (96, 200), (300, 520), (520, 300), (64, 64), (520, 296)]:
             mats.append((o, r, c))
-            o += r * c + 5
+            o = (o + r * c + 7) // 8 * 8 + 8
         self.s = Setup(mats, o, "bf16", "bf16", "bf16", gpu, seed=seed)
         g = torch.Generator(device=gpu)
         g.manual_seed(seed + 1)
@@ -37,10 +40,12 @@ class State:
         self.clip_ws = torch.empty(max(8, M.grad_norm_clip_workspace_size(2)), dtype=torch.uint8,
                                    device=gpu)
 
-    def step(self, hp, ahp):
+    def step(self, hp, ahp, with_out=True):
         s = self.s
         M.grad_norm_clip([s.grads, self.ag], 1.0, out=self.clip, workspace=self.clip_ws)
-        M.muon_step(s.plan, s.params, s.grads, s.mom, s.ws, hp, s.out, clip=self.clip)
+        # without out_update, the last NS phase applies the update itself
+        M.muon_step(s.plan, s.params, s.grads, s.mom, s.ws, hp, s.out if with_out else None,
+                    clip=self.clip)
         M.adamw_step(self.ap, self.am, self.ag, self.m, self.v, ahp, 1, clip=self.clip)
 
     def tensors(self):
@@ -48,13 +53,15 @@ class State:
         return [s.params, s.mom, s.out, self.ap, self.am, self.m, self.v, self.clip]
 
 
-def test_captured_step_replays_bitwise(gpu):
+@pytest.mark.parametrize("with_out", [True, False])
+def test_captured_step_replays_bitwise(gpu, with_out):
     hp, ahp = mhp(QUINTIC), W.AdamWHParams()
     eager = State(gpu, 21)
     assert eager.s.plan.info().small_mats == 3
+    assert eager.s.plan.info().fused_apply_mats == 2
     ref = []
     for _ in range(3):
-        eager.step(hp, ahp)
+        eager.step(hp, ahp, with_out)
         torch.cuda.synchronize()
         ref.append([t.clone() for t in eager.tensors()])
 
@@ -66,7 +73,7 @@ def test_captured_step_replays_bitwise(gpu):
     snapshot = [t.clone() for t in cap.tensors()]
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
-            cap.step(hp, ahp)
+            cap.step(hp, ahp, with_out)
     torch.cuda.synchronize()
     # capture does not run the work: restore the starting state anyway
     for t, s0 in zip(cap.tensors(), snapshot):
