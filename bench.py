@@ -98,6 +98,8 @@ def parse():
     ap.add_argument("--workload", default="dense_d2048_l16")
     ap.add_argument("--coef", default="quintic", choices=["quintic", "cubic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--adamw-stream", choices=["same", "side"], default="side",
+                    help="AdamW on the Muon stream, or on a second stream beside the NS kernels")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (counter scale)")
     return ap.parse_args()
@@ -194,6 +196,9 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    # AdamW does not depend on the Muon group: optionally on its own stream
+    # (default priority), joined back at the end of the step
+    side = torch.cuda.Stream() if args.adamw_stream == "side" else None
     n_waves = info.n_waves
     phases = (1, 2, 3) if hp.ns_c != 0.0 else (1, 3)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -203,19 +208,33 @@ def main():
         """One optimizer step; with ``record`` returns per-kernel event pairs."""
         marks = {"momentum": [], "ns1": [], "ns2": [], "ns3": [], "ns3_apply": [], "adamw": []}
 
-        def timed(key, fn):
+        def timed(key, fn, st=None):
+            st = stream if st is None else st
             if record:
                 a, b = ev(), ev()
-                a.record(stream)
+                a.record(st)
                 fn()
-                b.record(stream)
+                b.record(st)
                 marks[key].append((a, b))
             else:
                 fn()
 
+        def adamw_all():
+            for a in adam:
+                timed("adamw", lambda: M.adamw_step(a.param, a.master, a.grad, a.exp_avg,
+                                                    a.exp_avg_sq, ahp, t_step[0]),
+                      side)
+
+        t_step[0] += 1
         for w in range(n_waves):
             timed("momentum", lambda: M.muon_stage_momentum(plan, w, inp.grads, inp.momentum,
                                                             ws, hp))
+            if side is not None and w == 0:
+                # after the first (bandwidth-bound) momentum pass, beside the
+                # compute-bound NS kernels
+                side.wait_stream(stream)
+                with torch.cuda.stream(side):
+                    adamw_all()
             # the last phase 3 applies the update (as muon_step does)
             for it in range(hp.ns_steps):
                 for ph in phases:
@@ -224,10 +243,10 @@ def main():
                               lambda: M.muon_stage_ns_apply(plan, w, inp.params, ws, hp))
                     else:
                         timed(f"ns{ph}", lambda: M.muon_stage_ns_phase(plan, w, ws, hp, it, ph))
-        t_step[0] += 1
-        for a in adam:
-            timed("adamw", lambda: M.adamw_step(a.param, a.master, a.grad, a.exp_avg,
-                                                a.exp_avg_sq, ahp, t_step[0]))
+        if side is None:
+            adamw_all()
+        else:
+            stream.wait_stream(side)
         return marks
 
     for _ in range(args.warmup):
@@ -425,6 +444,7 @@ def main():
             "ns_dtype": "bf16",
             "param_dtype": wl.param_dtype,
             "waves": n_waves,
+            "adamw_stream": args.adamw_stream,
             "workspace_GiB": round(plan.workspace_bytes / 2 ** 30, 3),
         },
         "value_definition": "algorithmic NS flops of one step / whole optimizer step time",
