@@ -223,3 +223,14 @@ def test_longest_side_a_plan_accepts():
         for shape in ((1, longest + 1), (longest + 1, 1)):
             assert _err(ws, [(0, *shape)], longest + 1, nsd, nsd, nsd) == M.MUON_ERR_BAD_SHAPE
             assert "too large" in M.muon_last_error()
+
+
+def test_stage_ns_apply_validates_before_any_hip_call():
+    L = M.lib()
+    hp = M.MuonHParamsC()
+    fake = ctypes.c_void_p(4096)
+    assert L.muon_stage_ns_apply(None, 0, fake, fake, 1 << 20, ctypes.byref(hp), None) == \
+        M.MUON_ERR_INVALID_ARG
+    # plan info carries the count of matrices whose update the last NS phase applies
+    names = [f[0] for f in M.MuonPlanInfo._fields_]
+    assert names[-2:] == ["fused_apply_mats", "reserved"]

@@ -57,6 +57,9 @@ def test_muon_step_checks_buffers_against_the_plan():
     _err(lambda: M.muon_step(plan, P, G, Mo, torch.empty(4096, dtype=torch.uint8), hp),
          M.MUON_ERR_INVALID_ARG)  # workspace on the host
     _err(lambda: M.muon_stage_apply(plan, 0, FakeGpuTensor(5), W, hp), M.MUON_ERR_INVALID_ARG)
+    _err(lambda: M.muon_stage_ns_apply(plan, 0, FakeGpuTensor(5), W, hp), M.MUON_ERR_INVALID_ARG)
+    _err(lambda: M.muon_stage_ns_apply(plan, 0, FakeGpuTensor(1000, torch.float32), W, hp),
+         M.MUON_ERR_BAD_DTYPE)
     _err(lambda: M.muon_stage_momentum(plan, 0, G, FakeGpuTensor(999, torch.float32), W, hp),
          M.MUON_ERR_INVALID_ARG)
     _err(lambda: M.muon_stage_export_x(plan, 0, W, 0, FakeGpuTensor(999, torch.float32)),
