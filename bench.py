@@ -100,6 +100,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adamw-stream", choices=["same", "side"], default="side",
                     help="AdamW on the Muon stream, or on a second stream beside the NS kernels")
+    ap.add_argument("--adamw-beside", type=int, choices=[1, 2, 3], default=1,
+                    help="with a side stream: the NS phase of the first iteration AdamW starts with")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (counter scale)")
     return ap.parse_args()
@@ -229,15 +231,15 @@ def main():
         for w in range(n_waves):
             timed("momentum", lambda: M.muon_stage_momentum(plan, w, inp.grads, inp.momentum,
                                                             ws, hp))
-            if side is not None and w == 0:
-                # after the first (bandwidth-bound) momentum pass, beside the
-                # compute-bound NS kernels
-                side.wait_stream(stream)
-                with torch.cuda.stream(side):
-                    adamw_all()
             # the last phase 3 applies the update (as muon_step does)
             for it in range(hp.ns_steps):
                 for ph in phases:
+                    if side is not None and w == 0 and it == 0 and ph == args.adamw_beside:
+                        # after the (bandwidth-bound) momentum pass, beside
+                        # a compute-bound NS kernel
+                        side.wait_stream(stream)
+                        with torch.cuda.stream(side):
+                            adamw_all()
                     if ph == 3 and it == hp.ns_steps - 1:
                         timed("ns3_apply",
                               lambda: M.muon_stage_ns_apply(plan, w, inp.params, ws, hp))
@@ -445,6 +447,7 @@ def main():
             "param_dtype": wl.param_dtype,
             "waves": n_waves,
             "adamw_stream": args.adamw_stream,
+            "adamw_beside_phase": args.adamw_beside if args.adamw_stream == "side" else None,
             "workspace_GiB": round(plan.workspace_bytes / 2 ** 30, 3),
         },
         "value_definition": "algorithmic NS flops of one step / whole optimizer step time",
