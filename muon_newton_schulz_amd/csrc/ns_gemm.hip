@@ -12,6 +12,9 @@
 // On the first iteration s2 = inv^2 and xs = inv, which folds the
 // Frobenius normalisation X0 = U/(||U||_F + eps) into the epilogues.
 // X lives in two ping-pong buffers (m x n, row-major, zero padded).
+// The last phase 3 of a step can instead apply the update to the
+// parameters, W <- (1 - lr wd) W - lr s O with O the bf16 value X' would
+// hold (k_ns_bf16_apply; optimizer tutorial 3.1, decoupled decay).
 //
 // Phases 1 and 2 are "NT" products, C[i][j] = sum_k P[i][k] Q[j][k], with
 // both operands K-contiguous.  Phase 3 is "NN": P = B (K-contiguous rows),
