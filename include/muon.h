@@ -148,7 +148,8 @@ typedef struct {
   int32_t small_mats;         /* matrices on the fused small-matrix path (below) */
   int32_t split_diag_mats;    /* tiled bf16 matrices whose diagonal tiles of
                                  X X^T and A A compute only their upper blocks
-                                 (below) */
+                                 (below; all of them unless
+                                 MUON_PLAN_FULL_DIAG) */
   int32_t fused_apply_mats;   /* matrices whose update can be applied by the
                                  last phase 3 (muon_stage_ns_apply) */
   int32_t reserved;
@@ -177,12 +178,12 @@ int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_num
  * path.  MUON_PLAN_TILED_ONLY puts every matrix on the tiled path.
  *
  * X X^T and A A are symmetric: the tiled path computes the tiles on and
- * above the diagonal and mirrors them.  On a tiled bf16 matrix whose short
- * side pads to at most 8 tiles (2048), a diagonal tile also computes only
- * its upper 32x32 blocks and mirrors the rest; larger matrices compute whole
- * diagonal tiles (splitting them was measured slower there).  The result is
- * bitwise the same either way; MUON_PLAN_FULL_DIAG computes whole diagonal
- * tiles for every matrix. */
+ * above the diagonal and mirrors them.  On a tiled bf16 matrix a diagonal
+ * tile also computes only its upper 32x32 blocks and mirrors the rest; for
+ * a matrix whose short side pads to more than 8 tiles (2048) those tiles
+ * run after all off-diagonal tiles of the phase.  The result is bitwise the
+ * same either way; MUON_PLAN_FULL_DIAG computes whole diagonal tiles, in
+ * place, for every matrix. */
 #define MUON_PLAN_TILED_ONLY 1u
 #define MUON_PLAN_FULL_DIAG 2u
 int muon_plan_create_ex(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,

@@ -192,10 +192,7 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                d.m_k <= muon::kSmallM && (d.m_k / 32) * ((d.n_k + 127) / 128) <= 8)
                   ? 1
                   : 0;
-    d.diag = (ns_dtype == MUON_DTYPE_BF16 && !d.small && !(flags & MUON_PLAN_FULL_DIAG) &&
-              d.m_pad / T <= muon::kDiagMaxTiles)
-                 ? 1
-                 : 0;
+    d.diag = (ns_dtype == MUON_DTYPE_BF16 && !d.small && !(flags & MUON_PLAN_FULL_DIAG)) ? 1 : 0;
     // the fused update writes 16-byte pieces of 8 parameters along a
     // natural row
     d.fuse = (ns_dtype == MUON_DTYPE_BF16 && param_dtype == MUON_DTYPE_BF16 && !d.small &&
@@ -301,6 +298,12 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
       return p.mats[x].n_pad > p.mats[y].n_pad;
     });
     for (int m : order) emit_super_tiles(m, p.mats[m].m_pad / T, p.mats[m].m_pad / T, true, syrk_l);
+    // the split diagonal tiles of large matrices after all off-diagonal tiles
+    std::stable_partition(syrk_l.begin(), syrk_l.end(), [&](const Item& it) {
+      const MatDev& d = p.mats[it.mat];
+      return !(d.diag && d.m_pad / T > muon::kDiagInPlaceMaxTiles &&
+               (it.rc >> 16) == (it.rc & 0xffffu));
+    });
     std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
       return p.mats[x].m_pad > p.mats[y].m_pad;
     });

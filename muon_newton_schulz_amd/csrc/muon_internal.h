@@ -19,12 +19,11 @@ constexpr int kNsKStep = 32;  // bf16 engine: K per pipeline stage
 constexpr int kSmallM = 128;
 constexpr int kSmallElems = 32768;
 // Tiled bf16 NS: the diagonal tiles of A = X X^T and A A split their upper
-// blocks between the waves for matrices with at most this many tiles per
-// side of A (m_pad / kTileBf16); larger matrices compute full diagonal tiles.
-#ifndef MUON_DIAG_MAX_TILES
-#define MUON_DIAG_MAX_TILES 8
-#endif
-constexpr int kDiagMaxTiles = MUON_DIAG_MAX_TILES;
+// blocks between the waves.  A matrix with more than this many tiles per
+// side of A (m_pad / kTileBf16) has its diagonal tiles run after every
+// off-diagonal tile of the phase; a smaller one keeps them in place, next
+// to the tiles that share their operand panels.
+constexpr int kDiagInPlaceMaxTiles = 8;
 
 // One matrix of a plan, as the device sees it.  "Oriented" dims put the
 // short side first (m = min(rows, cols), n = max(rows, cols)); tall

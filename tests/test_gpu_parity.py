@@ -271,9 +271,9 @@ def test_small_matrix_kernel_is_bitwise_the_tiled_path(gpu, coef, pdt):
         assert torch.equal(a, b)
 
 
-# diagonal tiles of the symmetric products split into upper blocks for a
-# short side padded to at most 8 tiles (2048); (2304, 2400) has 9 and
-# computes whole diagonal tiles either way; (64, 64) is on the fused path
+# diagonal tiles of the symmetric products split into upper blocks; with a
+# short side padded to more than 8 tiles ((2304, 2400): 9) they run after
+# the off-diagonal tiles; (64, 64) is on the fused small-matrix path
 DIAG_SHAPES = [(2048, 2100), (2100, 2048), (300, 520), (520, 300), (1000, 700), (2304, 2400),
                (64, 64)]
 
@@ -283,7 +283,7 @@ def test_split_diagonal_tiles_are_bitwise_whole_tiles(gpu, coef):
     mats, n = _flat(DIAG_SHAPES)
     split = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=14)
     whole = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=14, full_diag=True)
-    assert split.plan.info().split_diag_mats == 5 and whole.plan.info().split_diag_mats == 0
+    assert split.plan.info().split_diag_mats == 6 and whole.plan.info().split_diag_mats == 0
     assert split.plan.info().small_mats == 1
     hp = mhp(coef)
     for _ in range(2):
