@@ -146,10 +146,8 @@ typedef struct {
   size_t workspace_bytes;
   double ns_flops_per_iter_alg;   /* algorithmic flops per NS iteration with c != 0 */
   int32_t small_mats;         /* matrices on the fused small-matrix path (below) */
-  int32_t split_diag_mats;    /* tiled bf16 matrices whose diagonal tiles of
-                                 X X^T and A A compute only their upper blocks
-                                 (below; all of them unless
-                                 MUON_PLAN_FULL_DIAG) */
+  int32_t split_tile_mats;    /* tiled bf16 matrices with split tiles (below;
+                                 all of them unless MUON_PLAN_WHOLE_TILES) */
   int32_t fused_apply_mats;   /* matrices whose update can be applied by the
                                  last phase 3 (muon_stage_ns_apply) */
   int32_t reserved;
@@ -178,14 +176,15 @@ int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_num
  * path.  MUON_PLAN_TILED_ONLY puts every matrix on the tiled path.
  *
  * X X^T and A A are symmetric: the tiled path computes the tiles on and
- * above the diagonal and mirrors them.  On a tiled bf16 matrix a diagonal
- * tile also computes only its upper 32x32 blocks and mirrors the rest; for
- * a matrix whose short side pads to more than 8 tiles (2048) those tiles
- * run after all off-diagonal tiles of the phase.  The result is bitwise the
- * same either way; MUON_PLAN_FULL_DIAG computes whole diagonal tiles, in
- * place, for every matrix. */
+ * above the diagonal and mirrors them.  On a tiled bf16 matrix (split
+ * tiles) a diagonal tile also computes only its upper 32x32 blocks and
+ * mirrors the rest; for a matrix whose short side pads to more than 8 tiles
+ * (2048) those tiles run after all off-diagonal tiles of the phase.  On a
+ * matrix of at most 8 tiles per side, an edge tile whose last 128 rows or
+ * columns are padding computes only the half that holds data.  The result is bitwise the same either way;
+ * MUON_PLAN_WHOLE_TILES computes every tile whole, in place. */
 #define MUON_PLAN_TILED_ONLY 1u
-#define MUON_PLAN_FULL_DIAG 2u
+#define MUON_PLAN_WHOLE_TILES 2u
 int muon_plan_create_ex(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                         int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
                         size_t workspace_cap, uint32_t flags, muon_plan_t** out,

@@ -100,7 +100,7 @@ class MuonPlanInfo(ctypes.Structure):
                 ("k1_tiles", ctypes.c_int64), ("syrk_tiles", ctypes.c_int64),
                 ("bx_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("ns_flops_per_iter_alg", ctypes.c_double), ("small_mats", ctypes.c_int32),
-                ("split_diag_mats", ctypes.c_int32), ("fused_apply_mats", ctypes.c_int32),
+                ("split_tile_mats", ctypes.c_int32), ("fused_apply_mats", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
 
 
@@ -302,14 +302,15 @@ def muon_workspace_size(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype
 
 
 MUON_PLAN_TILED_ONLY = 1
-MUON_PLAN_FULL_DIAG = 2
+MUON_PLAN_WHOLE_TILES = 2
 
 
 def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="bf16",
                      workspace_cap: int = 0, tiled_only: bool = False,
-                     full_diag: bool = False) -> MuonPlan:
+                     whole_tiles: bool = False) -> MuonPlan:
     """tiled_only: every matrix on the tiled NS path (no fused small-matrix
-    kernel); full_diag: whole diagonal tiles in the symmetric products.
+    kernel); whole_tiles: every NS tile computed whole (no split diagonal
+    or edge tiles).
     Results are bitwise the same either way."""
     arr = _mats_array(mats)
     h = ctypes.c_void_p(0)
@@ -318,7 +319,7 @@ def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="b
                                      dtype_code(grad_dtype), dtype_code(ns_dtype),
                                      int(workspace_cap),
                                      (MUON_PLAN_TILED_ONLY if tiled_only else 0)
-                                     | (MUON_PLAN_FULL_DIAG if full_diag else 0),
+                                     | (MUON_PLAN_WHOLE_TILES if whole_tiles else 0),
                                      ctypes.byref(h), ctypes.byref(ws)))
     return MuonPlan(h.value, ws.value, len(mats), int(flat_numel), dtype_code(param_dtype),
                     dtype_code(grad_dtype))

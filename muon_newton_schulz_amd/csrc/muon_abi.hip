@@ -128,7 +128,7 @@ void emit_super_tiles(int mat, int rows, int cols, bool tri, std::vector<Item>& 
 int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype, size_t workspace_cap,
                uint32_t flags, muon_plan& p) {
-  if ((flags & ~static_cast<uint32_t>(MUON_PLAN_TILED_ONLY | MUON_PLAN_FULL_DIAG)) != 0)
+  if ((flags & ~static_cast<uint32_t>(MUON_PLAN_TILED_ONLY | MUON_PLAN_WHOLE_TILES)) != 0)
     return fail(MUON_ERR_INVALID_ARG, "unknown plan flags");
   if (n_mats < 0) return fail(MUON_ERR_INVALID_ARG, "n_mats < 0");
   if (n_mats > 0 && mats == nullptr) return fail(MUON_ERR_INVALID_ARG, "mats is null");
@@ -192,7 +192,7 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                d.m_k <= muon::kSmallM && (d.m_k / 32) * ((d.n_k + 127) / 128) <= 8)
                   ? 1
                   : 0;
-    d.diag = (ns_dtype == MUON_DTYPE_BF16 && !d.small && !(flags & MUON_PLAN_FULL_DIAG)) ? 1 : 0;
+    d.split = (ns_dtype == MUON_DTYPE_BF16 && !d.small && !(flags & MUON_PLAN_WHOLE_TILES)) ? 1 : 0;
     // the fused update writes 16-byte pieces of 8 parameters along a
     // natural row
     d.fuse = (ns_dtype == MUON_DTYPE_BF16 && param_dtype == MUON_DTYPE_BF16 && !d.small &&
@@ -301,7 +301,7 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     // the split diagonal tiles of large matrices after all off-diagonal tiles
     std::stable_partition(syrk_l.begin(), syrk_l.end(), [&](const Item& it) {
       const MatDev& d = p.mats[it.mat];
-      return !(d.diag && d.m_pad / T > muon::kDiagInPlaceMaxTiles &&
+      return !(d.split && d.m_pad / T > muon::kDiagInPlaceMaxTiles &&
                (it.rc >> 16) == (it.rc & 0xffffu));
     });
     std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
@@ -524,10 +524,10 @@ int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {
   info->workspace_bytes = plan->ws_bytes;
   info->ns_flops_per_iter_alg = plan->flops_per_iter;
   info->small_mats = static_cast<int32_t>(plan->small_list.size());
-  info->split_diag_mats = 0;
+  info->split_tile_mats = 0;
   info->fused_apply_mats = 0;
   for (const muon::MatDev& d : plan->mats) {
-    info->split_diag_mats += d.diag;
+    info->split_tile_mats += d.split;
     info->fused_apply_mats += d.fuse;
   }
   info->reserved = 0;

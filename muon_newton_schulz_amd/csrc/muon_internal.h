@@ -41,8 +41,9 @@ struct MatDev {
   int32_t k1_begin;      // first elementwise tile of this matrix (wave-local)
   int32_t k1_count;      // number of elementwise tiles of this matrix
   int32_t small;         // 1: NS runs in the fused one-workgroup kernel
-  int32_t diag;          // 1: diagonal tiles of the symmetric products
-                         // compute only their upper blocks
+  int32_t split;         // 1: split tiles (diagonal tiles of the symmetric
+                         // products, half-empty edge tiles) share their
+                         // work out over the waves
   int32_t fuse;          // 1: the last phase 3 can apply the update to W in
                          // its epilogue (tiled bf16 NS, bf16 params, offset
                          // and cols multiples of 8)

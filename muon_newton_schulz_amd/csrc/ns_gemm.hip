@@ -196,16 +196,29 @@ __device__ __forceinline__ int stg(int i, int j) {
   return i * 128 + ((((j >> 2) ^ g) & 31) << 2);
 }
 
-// Diagonal tiles of the symmetric products (phases 1, 2) need only the 36
-// upper 32x32 blocks of their 8x8.  ROLE 1, waves (0,0) and (1,1): the upper
-// blocks of their quadrant (bi <= bj, 10 of 16).  ROLE 2: wave (0,1) the left
-// half of quadrant (0,1) (bj < 2, 8 blocks), wave (1,0) the same on Q rows
-// 64 further, i.e. that quadrant's right half.  Every wave writes its blocks
-// and, mirrored, their transposes, so a diagonal tile costs 10 MFMA slots
-// per substep instead of 16.  ROLE 0: the whole quadrant (every other tile).
-__device__ __forceinline__ int tile_role(int phase, int ti, int tj, int wave) {
-  if (phase == 3 || ti != tj) return 0;
-  return (wave == 0 || wave == 3) ? 1 : 2;
+// Split tiles.  Diagonal tiles of the symmetric products (phases 1, 2) need
+// only the 36 upper 32x32 blocks of their 8x8.  ROLE 1, waves (0,0) and
+// (1,1): the upper blocks of their quadrant (bi <= bj, 10 of 16).  ROLE 2:
+// wave (0,1) the left half of quadrant (0,1) (bj < 2, 8 blocks), wave (1,0)
+// the same on Q rows 64 further, i.e. that quadrant's right half.  Every
+// wave writes its blocks and, mirrored, their transposes, so a diagonal tile
+// costs 10 MFMA slots per substep instead of 16.
+// Edge tiles whose last 128 rows (ROLE 3, phase 3: the m side) or columns
+// (ROLE 4: the Q side) are all padding: the four waves split the two
+// quadrants that hold data, 64 Q rows each, as ROLE 2 splits one, so the
+// tile costs 8 MFMA slots per substep; only on matrices with at most
+// kDiagInPlaceMaxTiles tiles per side (on larger ones they measured
+// slower).  ROLE 0: the whole quadrant.  Only matrices with MatDev::split
+// take split tiles.
+__device__ __forceinline__ int tile_role(int phase, const MatDev& md, int ti, int tj, int wave) {
+  if (!md.split) return 0;
+  if (phase != 3 && ti == tj) return (wave == 0 || wave == 3) ? 1 : 2;
+  if (md.m_pad > kDiagInPlaceMaxTiles * BT) return 0;
+  const int m = md.rows < md.cols ? md.rows : md.cols;
+  const int n = md.rows < md.cols ? md.cols : md.rows;
+  if (phase == 3 && m - ti * BT <= BT / 2) return 3;
+  if ((phase == 3 ? n : m) - tj * BT <= BT / 2) return 4;
+  return 0;
 }
 
 // One 256x256 output tile: operand pipeline, MFMA main loop, epilogue.
@@ -215,7 +228,8 @@ template <int PHASE, int ROLE, bool APPLY = false>
 __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, const int ti,
                                         const int tj, const float inv, uint16_t* smem) {
   // MFMA m = 4 bj + bi runs iff bit m is set
-  constexpr uint32_t MASK = ROLE == 1 ? 0xF731u : ROLE == 2 ? 0x00FFu : 0xFFFFu;
+  constexpr uint32_t MASK = ROLE == 0 ? 0xFFFFu : ROLE == 1 ? 0xF731u : 0x00FFu;
+  static_assert(ROLE <= 2 || (ROLE == 3 ? PHASE == 3 : true), "half-height tiles are phase 3's");
   uint16_t* ws = static_cast<uint16_t*>(g.ws);
 
   // operands
@@ -245,11 +259,14 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wi = wave & 1, wj = wave >> 1;
   const int frow = lane & 31;
-  // quadrant this wave computes (wave (1,0) of a diagonal tile: quadrant
-  // (0,1), Q rows shifted by 64)
+  // quadrant this wave computes and the shift of its 64 Q rows: wave (1,0)
+  // of a diagonal tile takes quadrant (0,1) shifted by 64; on a half-height
+  // tile wave (wi, wj) takes quadrant (0, wj) shifted by 64 wi, on a
+  // half-width tile quadrant (wi, 0) shifted by 64 wj
   const bool adopt = ROLE == 2 && wi == 1;
-  const int wie = adopt ? 0 : wi, wje = adopt ? 1 : wj;
-  const int qshift = adopt ? 64 : 0;
+  const int wie = ROLE == 3 ? 0 : ROLE == 4 ? wi : adopt ? 0 : wi;
+  const int wje = ROLE == 3 ? wj : ROLE == 4 ? 0 : adopt ? 1 : wj;
+  const int qshift = ROLE == 3 ? 64 * wi : ROLE == 4 ? 64 * wj : adopt ? 64 : 0;
 
   // MFMA operand fragments.  A fragment set (one 16-wide k substep) is
   // NR LDS reads: 4 P fragments (ds_read_b128) then the Q fragments, 4
@@ -276,9 +293,11 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   {
     const int s = lane & 15, yy = (s >> 2) & 3;
     const int x = 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const int bq = qshift >> 5;  // 32-column blocks of the Q shift
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-      vt[b] = BT * BK * 2 + ((8 * (lane >> 5) + (s >> 2)) * BT + wj * 128 + x + ((b ^ yy) << 5)) * 2;
+      vt[b] = BT * BK * 2 +
+              ((8 * (lane >> 5) + (s >> 2)) * BT + wje * 128 + x + ((((b + bq) & 3) ^ yy) << 5)) * 2;
   }
   struct Frags {
     bf16x8_t p[4];
@@ -290,13 +309,14 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     if constexpr (R < 4) {
       f.p[R] = ld128_async<R * 32 * BK * 2>(vp[KS] + sb);
     } else if constexpr (PHASE != 3) {
-      // ROLE 2 uses Q fragments 0 and 1 only (the others would lie past
-      // the shifted wave's Q rows)
-      if constexpr (ROLE != 2 || R - 4 < 2)
+      // split roles use Q fragments 0 and 1 only (the others would lie
+      // past the shifted wave's Q rows)
+      if constexpr (ROLE < 2 || R - 4 < 2)
         f.q[R - 4] = ld128_async<(R - 4) * 32 * BK * 2>(vq[KS] + sb);
     } else {
       constexpr int B = (R - 4) >> 1, H = (R - 4) & 1;
-      f.t[R - 4] = ld_tr_async<KS * 16 * BT * 2 + H * 4 * BT * 2>(vt[B] + sb);
+      if constexpr (ROLE < 2 || B < 2)
+        f.t[R - 4] = ld_tr_async<KS * 16 * BT * 2 + H * 4 * BT * 2>(vt[B] + sb);
     }
   };
   // all reads of a set have landed (no other LDS reads outstanding)
@@ -452,10 +472,11 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
       // past W's rows or cols is not loaded (cols is a multiple of 8)
       const int pl = opaque_lane(lane);
       const int wc = j0w + 8 * (pl & 15);
+      const bool wcol = wc < md.cols && (ROLE < 2 || (pl & 15) < 8);
 #pragma unroll
       for (int u = 0; u < 32; ++u) {
         const int wr = i0w + (pl >> 4) + 4 * u;
-        if (wr < md.rows && wc < md.cols)
+        if (wr < md.rows && wcol)
           apre[u] = *reinterpret_cast<const u32x4_t*>(Wm + static_cast<int64_t>(wr) * md.cols + wc);
       }
     }
@@ -511,6 +532,8 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // 8*(lane/32) (the transposed pass's pieces).  cols is a multiple of 8, so
   // a piece is inside W or outside it whole.
   auto w_piece = [&](int u, int64_t& e) {
+    // a split-role wave computed staged columns 0..63 only
+    if (ROLE >= 2 && (md.trans ? (u & 3) >= 2 : rc >= 8)) return false;
     int wr, wc;
     if (!md.trans) {
       wr = i0w + (elane >> 4) + 4 * u;
@@ -634,12 +657,12 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 
   // row stores: 16 bytes per lane, 4 rows of 256 bytes per instruction;
   // ROLE 1 stores its upper blocks (block row r/32 <= block column rc/4),
-  // ROLE 2 staged columns 0..63 (j0w includes the Q shift)
+  // ROLES 2-4 staged columns 0..63 (j0w includes the Q shift)
 #pragma unroll 8
   for (int u = 0; u < 32; ++u) {
     const int r = (elane >> 4) + 4 * u;
     if (ROLE == 1 && (r >> 5) > (rc >> 2)) continue;
-    if (ROLE == 2 && rc >= 8) continue;
+    if (ROLE >= 2 && rc >= 8) continue;
     u32x4_t v = *reinterpret_cast<const u32x4_t*>(S + row_slot16(u));
     if (u & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
     *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(i0w + r) * ldc + j0w + 8 * rc) = v;
@@ -710,10 +733,11 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g, const Item* __re
     if (busy) __syncthreads();  // the previous tile's epilogue is done with LDS
     busy = true;
     const int ti = it.rc >> 16, tj = it.rc & 0xffff;
-    const int role =
-        md.diag ? tile_role(PHASE, ti, tj, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) : 0;
+    const int role = tile_role(PHASE, md, ti, tj, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
     if (PHASE != 3 && role == 1) ns_tile<PHASE, 1>(g, md, ti, tj, inv, smem);
     else if (PHASE != 3 && role == 2) ns_tile<PHASE, 2>(g, md, ti, tj, inv, smem);
+    else if (PHASE == 3 && role == 3) ns_tile<3, 3>(g, md, ti, tj, inv, smem);
+    else if (role == 4) ns_tile<PHASE, 4>(g, md, ti, tj, inv, smem);
     else ns_tile<PHASE, 0>(g, md, ti, tj, inv, smem);
   }
 }
@@ -732,7 +756,11 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16_apply(GemmArgs g, const Item
     const float inv = g.first ? invs[md.widx] : 1.0f;
     if (busy) __syncthreads();  // the previous tile's epilogue is done with LDS
     busy = true;
-    ns_tile<3, 0, true>(g, md, it.rc >> 16, it.rc & 0xffff, inv, smem);
+    const int ti = it.rc >> 16, tj = it.rc & 0xffff;
+    const int role = tile_role(3, md, ti, tj, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    if (role == 3) ns_tile<3, 3, true>(g, md, ti, tj, inv, smem);
+    else if (role == 4) ns_tile<3, 4, true>(g, md, ti, tj, inv, smem);
+    else ns_tile<3, 0, true>(g, md, ti, tj, inv, smem);
   }
 }
 

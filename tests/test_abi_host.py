@@ -204,7 +204,7 @@ def test_plan_flags_validate_before_any_hip_call():
     def rc(flags):
         return L.muon_plan_create_ex(mats, 1, 64, 1, 1, 1, 0, flags, ctypes.byref(h),
                                      ctypes.byref(ws))
-    assert M.MUON_PLAN_TILED_ONLY == 1 and M.MUON_PLAN_FULL_DIAG == 2
+    assert M.MUON_PLAN_TILED_ONLY == 1 and M.MUON_PLAN_WHOLE_TILES == 2
     assert rc(4) == M.MUON_ERR_INVALID_ARG
     assert rc(1 << 31) == M.MUON_ERR_INVALID_ARG
     # the known flags pass validation and the call gets as far as the device

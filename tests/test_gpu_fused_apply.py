@@ -36,6 +36,8 @@ SHAPES = [
     (2048, 5632, True),
     (5632, 2048, True),
     (300, 520, True),     # offset made odd below: not fused
+    (330, 1024, True),    # wide, last tile row half padding (half-height tiles)
+    (256, 1096, True),    # wide, last tile column half padding (half-width tiles)
 ]
 
 
@@ -69,7 +71,7 @@ def test_fused_step_is_bitwise_the_apply_kernel(gpu, coef):
     mats, n, n_fused = _layout(SHAPES)
     a = Case(gpu, mats, n, 5)
     b = Case(gpu, mats, n, 5)
-    assert a.plan.info().fused_apply_mats == n_fused == 6
+    assert a.plan.info().fused_apply_mats == n_fused == 8
     hp = mhp(coef)
     p0 = a.params.clone()
     for _ in range(2):  # the second step starts from a nonzero momentum

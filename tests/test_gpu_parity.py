@@ -54,7 +54,7 @@ class Setup:
 
     def __init__(self, mats, n, param_dtype, grad_dtype, ns_dtype, dev, seed=0,
                  w_std=1.0, g_std=1.0, cap=0, sentinel=True, tiled_only=False,
-                 full_diag=False):
+                 whole_tiles=False):
         self.mats, self.n = mats, n
         self.param_dtype, self.ns_dtype = param_dtype, ns_dtype
         g = torch.Generator(device=dev)
@@ -70,7 +70,7 @@ class Setup:
                 self.grads.dtype)
             self.mom[o:o + r * c] = 0.0
         self.plan = M.muon_plan_create(mats, n, param_dtype, grad_dtype, ns_dtype, cap,
-                                       tiled_only=tiled_only, full_diag=full_diag)
+                                       tiled_only=tiled_only, whole_tiles=whole_tiles)
         self.ws = self.plan.alloc_workspace(dev)
         self.out = torch.full((n,), fill, dtype=torch.float32, device=dev)
 
@@ -282,8 +282,8 @@ DIAG_SHAPES = [(2048, 2100), (2100, 2048), (300, 520), (520, 300), (1000, 700), 
 def test_split_diagonal_tiles_are_bitwise_whole_tiles(gpu, coef):
     mats, n = _flat(DIAG_SHAPES)
     split = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=14)
-    whole = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=14, full_diag=True)
-    assert split.plan.info().split_diag_mats == 6 and whole.plan.info().split_diag_mats == 0
+    whole = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=14, whole_tiles=True)
+    assert split.plan.info().split_tile_mats == 6 and whole.plan.info().split_tile_mats == 0
     assert split.plan.info().small_mats == 1
     hp = mhp(coef)
     for _ in range(2):
