@@ -11,7 +11,8 @@
 //   phase 3  X' = xs * (B X)         the a X term is folded into B's diagonal
 // On the first iteration s2 = inv^2 and xs = inv, which folds the
 // Frobenius normalisation X0 = U/(||U||_F + eps) into the epilogues.
-// X lives in two ping-pong buffers (m x n, row-major, zero padded).
+// X lives in two ping-pong buffers (m x n, row-major, padded; the padding
+// inside the contraction extents m_k, n_k is zero).
 // The last phase 3 of a step can instead apply the update to the
 // parameters, W <- (1 - lr wd) W - lr s O with O the bf16 value X' would
 // hold (k_ns_bf16_apply; optimizer tutorial 3.1, decoupled decay).
