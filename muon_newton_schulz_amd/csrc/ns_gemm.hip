@@ -113,15 +113,16 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 // Wait until this wave's DMA for stage `st` has landed, given that stages
-// up to `newest` have been issued (DMA_PER_STAGE instructions each); the
-// newer stages may stay in flight (vmcnt counts vector memory
-// instructions, which complete in issue order).
+// up to `newest` have been issued (DPS instructions each); the newer
+// stages may stay in flight (vmcnt counts vector memory instructions,
+// which complete in issue order).
+template <int DPS>
 __device__ __forceinline__ void wait_stage_landed(int st, int newest) {
+  static_assert(NSLOT == 4, "wait counts below assume at most 3 newer stages");
   const int newer = newest - st;
-  static_assert(DMA_PER_STAGE == 8, "wait counts below assume 8 DMA per stage");
-  if (newer >= 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if (newer == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (newer == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if (newer >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * DPS) : "memory");
+  else if (newer == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPS) : "memory");
+  else if (newer == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DPS) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -265,6 +266,11 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // tile wave (wi, wj) takes quadrant (0, wj) shifted by 64 wi, on a
   // half-width tile quadrant (wi, 0) shifted by 64 wj
   const bool adopt = ROLE == 2 && wi == 1;
+  // A diagonal tile's P and Q panels are the same rows (ti == tj): in phase
+  // 2 it loads them once and reads its Q fragments from the P copy, with
+  // half the DMA.
+  constexpr bool SHARED_PQ = PHASE == 2 && (ROLE == 1 || ROLE == 2);
+  constexpr int DPS = SHARED_PQ ? DMA_PER_STAGE / 2 : DMA_PER_STAGE;  // DMA per wave per stage
   const int wie = ROLE == 3 ? 0 : ROLE == 4 ? wi : adopt ? 0 : wi;
   const int wje = ROLE == 3 ? wj : ROLE == 4 ? 0 : adopt ? 1 : wj;
   const int qshift = ROLE == 3 ? 64 * wi : ROLE == 4 ? 64 * wj : adopt ? 64 : 0;
@@ -284,7 +290,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   for (int ks = 0; ks < 2; ++ks) {
     const int sw = ((ks * 2 + (lane >> 5)) ^ ((frow >> 2) & 3)) << 3;
     vp[ks] = ((wie * 128 + frow) * BK + sw) * 2;
-    vq[ks] = BT * BK * 2 + ((wje * 128 + qshift + frow) * BK + sw) * 2;
+    vq[ks] = (SHARED_PQ ? 0 : BT * BK * 2) + ((wje * 128 + qshift + frow) * BK + sw) * 2;
   }
   // phase 3: transposed reads of column block b.  Lane group of 16: k row
   // 8*(lane/32) + (lane%16)/4 (+4 for the hi half, +16 per substep), columns
@@ -357,6 +363,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     dQ3[par] = ((lane >> 5) * ldq + 8 * ((lane & 31) ^ (((2 * par + (lane >> 5)) & 3) << 2))) * 2;
   auto issue_dma = [&](int kt, int slot, auto d_c) {
     constexpr int D = decltype(d_c)::value, U = D & 3;
+    if constexpr (D >= DPS) return;  // shared P and Q: no Q copy
     uint16_t* sp = smem + slot * 2 * BT * BK;
     uint16_t* sq = sp + BT * BK;
     const int64_t k0 = static_cast<int64_t>(kt) * BK;
@@ -385,7 +392,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 #pragma unroll
   for (int s0 = 0; s0 < NSLOT - 1; ++s0)
     if (s0 < nk) static_for<0, DMA_PER_STAGE>([&](auto d) { issue_dma(s0, s0, d); });
-  wait_stage_landed(0, min(NSLOT - 2, nk - 1));
+  wait_stage_landed<DPS>(0, min(NSLOT - 2, nk - 1));
   pipe_barrier();
 
   Frags F[2];
@@ -410,7 +417,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     if constexpr (NEXT) {
       // (the last stage has no next stage to wait for, and no slot is
       // refilled after it)
-      wait_stage_landed(kt + 1, min(kt + NSLOT - 2, nk - 1));
+      wait_stage_landed<DPS>(kt + 1, min(kt + NSLOT - 2, nk - 1));
       pipe_barrier();
     }
     settle(F[1]);
