@@ -112,8 +112,8 @@ typedef struct {
   int32_t scale_mode;
   float rms_target;
   /* nullable device pointer: gradient scale and step guard from
-   * grad_norm_clip; read by muon_step, muon_stage_momentum (scale, skip)
-   * and muon_stage_apply (skip) */
+   * grad_norm_clip; read by muon_step, muon_stage_momentum (scale, skip),
+   * muon_stage_apply and muon_stage_ns_apply (skip) */
   const muon_clip_state_t* clip;
 } muon_hparams_t;
 
@@ -215,7 +215,10 @@ int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* m
 /* The stages muon_step enqueues, exposed for stepwise checks and timing.
  * muon_step(...) == for each wave w: muon_stage_momentum(w);
  *   for it in [0, ns_steps): for phase in {1, 2 (only if ns_c != 0), 3}:
- *   muon_stage_ns_phase(w, it, phase); muon_stage_apply(w).
+ *   muon_stage_ns_phase(w, it, phase); muon_stage_apply(w); without
+ *   out_update the last phase 3 and the apply are muon_stage_ns_apply(w).
+ *   (muon_step runs the small matrices' iterations in one launch; the
+ *   stage calls run one per phase-3 call; the results are bitwise equal.)
  * Phase 1: A = X X^T; phase 2: B = b A + c A A; phase 3: X <- a X + B X
  * (with c == 0, phase 3 uses b A for B).  The apply step is
  * W <- (1 - lr wd) W - lr s O with s the update scale of scale_mode
