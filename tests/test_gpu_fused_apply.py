@@ -161,3 +161,26 @@ def test_dense_stack_fused_full_size(gpu):
         del inp, ws, out
         torch.cuda.empty_cache()
     assert torch.equal(res[0], res[1])
+
+
+def test_one_plan_two_streams_concurrently(gpu):
+    """A plan is immutable and shareable: two steps on two streams, each
+    with its own workspace and buffers, running at the same time, give
+    bitwise what each gives alone (no state hidden in the plan or library)."""
+    mats, n, _ = _layout(SHAPES)
+    hp = mhp(QUINTIC)
+    ref = [Case(gpu, mats, n, 40 + k) for k in range(2)]
+    for c in ref:
+        M.muon_step(c.plan, c.params, c.grads, c.mom, c.ws, hp)
+        torch.cuda.synchronize()
+    run = [Case(gpu, mats, n, 40 + k) for k in range(2)]
+    plan = run[0].plan                  # one plan for both streams
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for c, s in zip(run, streams):
+        with torch.cuda.stream(s):
+            M.muon_step(plan, c.params, c.grads, c.mom, c.ws, hp)
+    torch.cuda.synchronize()
+    for c, r in zip(run, ref):
+        assert torch.equal(c.params.view(torch.int16), r.params.view(torch.int16))
+        assert torch.equal(c.mom, r.mom)
