@@ -36,6 +36,10 @@
  *   - Buffers passed to one call must not alias each other.
  *   - Non-finite inputs propagate into the outputs unless the step is
  *     guarded through a clip state (grad_norm_clip below).
+ *   - Muon normalises U inside its first products, which accumulate the
+ *     unnormalised U U^T in fp32: a step is in range while
+ *     n * max|u|^2 < 3.4e38 (n the long side; |u| below about 1e17 for
+ *     n <= 1e4).
  */
 #ifndef MUON_H_
 #define MUON_H_

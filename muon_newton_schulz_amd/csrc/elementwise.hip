@@ -53,7 +53,7 @@ template <> struct Elem<_Float16> {
   }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -112,11 +112,11 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
                                                   const Item* __restrict__ items,
                                                   const GT* __restrict__ grads,
                                                   float* __restrict__ mom, UT* __restrict__ ws,
-                                                  float* __restrict__ partials, float mu,
+                                                  double* __restrict__ partials, float mu,
                                                   int nesterov, int bufs_aligned,
                                                   const ClipState* __restrict__ clip) {
   __shared__ float tile[kEwTile][kEwTile + 1];
-  __shared__ float wsum[4];
+  __shared__ double wsum[4];
   // guarded step: skip it whole, or scale the gradient (uniform branch)
   float gscale = 1.0f;
   if (clip != nullptr) {
@@ -129,7 +129,9 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
   const NatDims nd = nat_dims(md);
   UT* X = ws + md.ws_x[0];
   const float omm = 1.0f - mu;
-  float ss = 0.0f;
+  // the sum of squares in fp64 (fixed order), so the norm keeps full
+  // precision over the tile
+  double ss = 0.0;
   if (vec4_ok(md, bufs_aligned)) {
     const int cg = (threadIdx.x & 15) * 4, rg = threadIdx.x >> 4;
     const int c = c0 + cg;
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
         u = nesterov ? mu * m + omm * g : m;
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) ss = fmaf(u[k], u[k], ss);
+      for (int k = 0; k < 4; ++k) ss = fma(static_cast<double>(u[k]), static_cast<double>(u[k]), ss);
       if (md.trans) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) tile[rr][cg + k] = u[k];
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
         mom[e] = m;
         u = nesterov ? mu * m + omm * g : m;
       }
-      ss = fmaf(u, u, ss);
+      ss = fma(static_cast<double>(u), static_cast<double>(u), ss);
       if (md.trans) tile[rr][lc] = u;
       else Elem<UT>::st(X, static_cast<int64_t>(r) * nd.cp + c, u);
     }
@@ -229,7 +231,7 @@ __device__ __forceinline__ f32x16_t load_nat_tile(const MatDev& md, const UT* X,
 
 __global__ __launch_bounds__(256) void k_norm_finalize(const MatDev* __restrict__ mats,
                                                        int mat_begin,
-                                                       const float* __restrict__ partials,
+                                                       const double* __restrict__ partials,
                                                        float* __restrict__ norms,
                                                        float* __restrict__ inv, float eps) {
   __shared__ double red[256];
@@ -537,7 +539,7 @@ hipError_t adamw_states(int m_dtype, int v_dtype, void* params, float* master, c
 
 hipError_t launch_momentum(const MatDev* mats, const Item* items, int n_items, int grad_dtype,
                            int ns_dtype, const void* grads, float* mom, void* ws,
-                           float* partials, float mu, int nesterov, const ClipState* clip,
+                           double* partials, float mu, int nesterov, const ClipState* clip,
                            hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items), block(256);
@@ -555,7 +557,7 @@ hipError_t launch_momentum(const MatDev* mats, const Item* items, int n_items, i
 }
 
 hipError_t launch_norm_finalize(const MatDev* mats, int mat_begin, int n_mats,
-                                const float* partials, float* norms, float* inv, float eps,
+                                const double* partials, float* norms, float* inv, float eps,
                                 hipStream_t s) {
   if (n_mats == 0) return hipSuccess;
   hipLaunchKernelGGL(k_norm_finalize, dim3(n_mats), dim3(256), 0, s, mats, mat_begin, partials,

@@ -210,8 +210,9 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     return (rp / muon::kEwTile) * (cp / muon::kEwTile);
   };
   auto fixed_bytes = [&](int64_t k1, int64_t nm) {
-    // partial sums (one per k1 tile), norms and inverse norms (one per matrix)
-    return align_up(static_cast<size_t>(k1) * 4, kAlign) +
+    // fp64 partial sums (one per k1 tile), fp32 norms and inverse norms
+    // (one per matrix)
+    return align_up(static_cast<size_t>(k1) * 8, kAlign) +
            2 * align_up(static_cast<size_t>(nm) * 4, kAlign);
   };
   {
@@ -248,7 +249,7 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     for (int m = w.mat_begin; m < w.mat_end; ++m) k1 += k1_tiles_of(p.mats[m]);
     size_t off = 0;
     w.partial_off = off;
-    off += align_up(static_cast<size_t>(k1) * 4, kAlign);
+    off += align_up(static_cast<size_t>(k1) * 8, kAlign);
     w.norm_off = off;
     off += align_up(static_cast<size_t>(nm) * 4, kAlign);
     w.inv_off = off;
@@ -543,7 +544,7 @@ int muon_stage_momentum(const muon_plan_t* plan, int32_t wave, const void* grads
   if (grads == nullptr || momentum == nullptr)
     return fail(MUON_ERR_INVALID_ARG, "grads or momentum is null");
   const Wave& w = plan->waves[wave];
-  float* partials = reinterpret_cast<float*>(ws_bytes_ptr(workspace, w.partial_off));
+  double* partials = reinterpret_cast<double*>(ws_bytes_ptr(workspace, w.partial_off));
   hipError_t e = muon::launch_momentum(plan->d_mats, plan->d_k1 + w.k1_begin,
                                        static_cast<int>(w.k1_count), plan->grad_dtype,
                                        plan->ns_dtype, grads, momentum, workspace, partials,

@@ -97,10 +97,10 @@ struct GemmArgs {
 // kernel launchers (defined in the .hip files)
 hipError_t launch_momentum(const MatDev* mats, const Item* items, int n_items,
                            int grad_dtype, int ns_dtype, const void* grads, float* mom,
-                           void* ws, float* partials, float mu, int nesterov,
+                           void* ws, double* partials, float mu, int nesterov,
                            const ClipState* clip, hipStream_t s);
 hipError_t launch_norm_finalize(const MatDev* mats, int mat_begin, int n_mats,
-                                const float* partials, float* norms, float* inv,
+                                const double* partials, float* norms, float* inv,
                                 float eps, hipStream_t s);
 hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int param_dtype,
                         int ns_dtype, void* params, const void* ws, const float* inv,

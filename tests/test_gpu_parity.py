@@ -533,3 +533,17 @@ def test_ragged_shapes_full_size_sampled(gpu):
     small = sorted(range(40), key=lambda i: min(shapes[i]))
     sample = sorted(set([i for i in small if i % 10 == 0][:2] + small[:2]))
     _workload_sampled(gpu, "ragged_500", sample, mhp(QUINTIC), first=40)
+
+
+@pytest.mark.parametrize("g_std", [1e14, 1e-25])
+def test_extreme_gradient_scales_normalise_like_the_oracle(gpu, g_std):
+    # |u| ~ 1e13: n max|u|^2 ~ 1e29, inside the fp32 range that the first
+    # products (which see the unnormalised U) need; |u| ~ 1e-26: u^2
+    # underflows fp32, and ||U||_F then sits far below eps on both sides.
+    # Tiled and fused small-matrix paths, both NS dtypes.
+    mats, n = _flat([(300, 520), (520, 300), (96, 200), (64, 64)])
+    for nsd, pdt in (("bf16", "bf16"), ("fp32", "fp32")):
+        s = Setup(mats, n, pdt, pdt, nsd, gpu, seed=17, w_std=0.02, g_std=g_std)
+        worst = check_muon_step(s, mhp(QUINTIC))
+        assert np.isfinite(np64(s.out)).all() and np.isfinite(np64(s.params)).all()
+        assert worst["O"] <= TOL_O[nsd]
