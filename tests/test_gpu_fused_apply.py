@@ -83,6 +83,21 @@ def test_fused_step_is_bitwise_the_apply_kernel(gpu, coef):
     assert not torch.equal(a.params, p0)
 
 
+@pytest.mark.parametrize("steps", [0, 1, 2])
+def test_fused_step_few_iterations(gpu, steps):
+    # one iteration: the fused epilogue also applies the 1/||U|| scale of
+    # the first iteration; none: nothing to fuse, the apply kernel runs
+    mats, n, _ = _layout(SHAPES)
+    a = Case(gpu, mats, n, 12)
+    b = Case(gpu, mats, n, 12)
+    hp = mhp(QUINTIC, steps=steps)
+    M.muon_step(a.plan, a.params, a.grads, a.mom, a.ws, hp)
+    M.muon_step(b.plan, b.params, b.grads, b.mom, b.ws, hp, b.out)
+    torch.cuda.synchronize()
+    assert torch.equal(a.params.view(torch.int16), b.params.view(torch.int16))
+    assert torch.equal(a.mom, b.mom)
+
+
 def test_stage_ns_apply_composes_like_the_step(gpu):
     mats, n, _ = _layout(SHAPES)
     a = Case(gpu, mats, n, 6)
