@@ -271,6 +271,11 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // half the DMA.
   constexpr bool SHARED_PQ = PHASE == 2 && (ROLE == 1 || ROLE == 2);
   constexpr int DPS = SHARED_PQ ? DMA_PER_STAGE / 2 : DMA_PER_STAGE;  // DMA per wave per stage
+  // Half edge tiles: waves 2 and 3 load the padding half of P (half-height,
+  // phase 3) or of Q (half-width, phases 1 and 2), which no MFMA reads, so
+  // they skip those DMA and wait on half the count.
+  constexpr bool HALF_DMA = ROLE == 3 || (ROLE == 4 && PHASE != 3);
+  const bool dma_half = HALF_DMA && wave >= 2;
   const int wie = ROLE == 3 ? 0 : ROLE == 4 ? wi : adopt ? 0 : wi;
   const int wje = ROLE == 3 ? wj : ROLE == 4 ? 0 : adopt ? 1 : wj;
   const int qshift = ROLE == 3 ? 64 * wi : ROLE == 4 ? 64 * wj : adopt ? 64 : 0;
@@ -364,6 +369,8 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   auto issue_dma = [&](int kt, int slot, auto d_c) {
     constexpr int D = decltype(d_c)::value, U = D & 3;
     if constexpr (D >= DPS) return;  // shared P and Q: no Q copy
+    if constexpr (HALF_DMA && ((ROLE == 3) == (D < 4)))
+      if (dma_half) return;  // padding rows of P (ROLE 3) or Q (ROLE 4)
     uint16_t* sp = smem + slot * 2 * BT * BK;
     uint16_t* sq = sp + BT * BK;
     const int64_t k0 = static_cast<int64_t>(kt) * BK;
@@ -392,7 +399,11 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 #pragma unroll
   for (int s0 = 0; s0 < NSLOT - 1; ++s0)
     if (s0 < nk) static_for<0, DMA_PER_STAGE>([&](auto d) { issue_dma(s0, s0, d); });
-  wait_stage_landed<DPS>(0, min(NSLOT - 2, nk - 1));
+  auto wait_landed = [&](int st, int newest) {
+    if (HALF_DMA && dma_half) wait_stage_landed<DPS / 2>(st, newest);
+    else wait_stage_landed<DPS>(st, newest);
+  };
+  wait_landed(0, min(NSLOT - 2, nk - 1));
   pipe_barrier();
 
   Frags F[2];
@@ -417,7 +428,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     if constexpr (NEXT) {
       // (the last stage has no next stage to wait for, and no slot is
       // refilled after it)
-      wait_stage_landed<DPS>(kt + 1, min(kt + NSLOT - 2, nk - 1));
+      wait_landed(kt + 1, min(kt + NSLOT - 2, nk - 1));
       pipe_barrier();
     }
     settle(F[1]);
