@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void k_norm_finalize(const MatDev* __restrict_
   __syncthreads();
 #pragma unroll
   for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
   if (threadIdx.x == 0) {

@@ -198,7 +198,7 @@ __device__ __forceinline__ Stats block_stats(Stats s) {
   __syncthreads();
 #pragma unroll
   for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) sh[threadIdx.x] = stats_merge(sh[threadIdx.x], sh[threadIdx.x + w]);
+    if (static_cast<int>(threadIdx.x) < w) sh[threadIdx.x] = stats_merge(sh[threadIdx.x], sh[threadIdx.x + w]);
     __syncthreads();
   }
   return sh[0];
