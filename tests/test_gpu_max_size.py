@@ -1,6 +1,7 @@
 """Parity at the largest shapes, against the fp64 oracle: 8192-sided
 matrices (the largest Muon matrices of the ragged workload) on the tiled
-engine, and vectors at the longest side a plan accepts.
+engine, vectors at the longest side a plan accepts, and AdamW over the
+ragged workload's 1.17e9-element embedding and past 2^31 elements.
 
 The oracle cannot run NS on an 8192 x 8192 matrix in seconds, so the big
 matrices get an embedded input: the gradient is zero outside a scattered
@@ -129,4 +130,63 @@ def test_vector_at_the_longest_side(gpu, shape):
     # untouched head and tail
     assert np.all(np64(out[:3]) == 7.0) and np.all(np64(out[3 + r * c:]) == 7.0)
     del ws
+    torch.cuda.empty_cache()
+
+
+def _adam_check(p_got, master_got, m_got, v_got, p0, m0, g, hp, pdt):
+    """Oracle step on sampled elements; tolerances as for the other AdamW
+    parity tests (2e-6 relative on the states and master, bf16 params the
+    cast of the GPU's own master)."""
+    from test_gpu_parity import adam_oracle_run
+    pr, mr_, er, vr = adam_oracle_run(p0, m0, [g], hp, pdt)
+    assert rel(v_got, vr) <= 2e-6 and rel(m_got, er) <= 2e-6
+    if master_got is not None:
+        assert rel(master_got, mr_) <= 2e-6
+        np.testing.assert_array_equal(p_got, O.bf16_round(master_got))
+    else:
+        assert rel(p_got, pr) <= 2e-6
+
+
+def test_adamw_ragged_embedding_group_full_size(gpu):
+    # the 163840 x 7168 embedding of the ragged workload (1.17e9 bf16
+    # params, fp32 master): head, middle and tail sampled
+    from muon_newton_schulz_amd import workloads as W
+    wl = W.workload("ragged_500")
+    gi = max(range(len(wl.adam)), key=lambda i: wl.adam[i].numel)
+    grp = wl.adam[gi]
+    assert grp.numel == 163840 * 7168 and grp.master
+    a = W.make_adam_inputs(wl, gi, device=gpu)
+    g = W.make_adam_grad(wl, gi, 1, device=gpu)
+    n = grp.numel
+    samples = [slice(0, 4099), slice(n // 2 - 3001, n // 2 + 3001), slice(n - 4099, n)]
+    before = [(np64(a.param[s]), np64(a.master[s]), np64(g[s])) for s in samples]
+    M.adamw_step(a.param, a.master, g, a.exp_avg, a.exp_avg_sq, wl.adam_hp, 1)
+    torch.cuda.synchronize()
+    for s, (p0, m0, gg) in zip(samples, before):
+        _adam_check(np64(a.param[s]), np64(a.master[s]), np64(a.exp_avg[s]),
+                    np64(a.exp_avg_sq[s]), p0, m0, gg, wl.adam_hp, "bf16")
+    del a, g
+    torch.cuda.empty_cache()
+
+
+def test_adamw_past_2_31_elements(gpu):
+    # fp32 params without master, 2^31 + 12345 elements: the kernel's
+    # element indices pass 2^31 (64-bit indexing), sampled around it and at
+    # the tail
+    from muon_newton_schulz_amd import workloads as W
+    n = (1 << 31) + 12345
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(23)
+    p = torch.randn(n, generator=gen, device=gpu)
+    g = torch.randn(n, generator=gen, device=gpu).to(torch.bfloat16)
+    m = torch.zeros(n, device=gpu)
+    v = torch.zeros(n, device=gpu)
+    hp = W.AdamWHParams()
+    samples = [slice(0, 1000), slice((1 << 31) - 2000, (1 << 31) + 2000), slice(n - 1000, n)]
+    before = [(np64(p[s]), np64(g[s])) for s in samples]
+    M.adamw_step(p, None, g, m, v, hp, 1)
+    torch.cuda.synchronize()
+    for s, (p0, gg) in zip(samples, before):
+        _adam_check(np64(p[s]), None, np64(m[s]), np64(v[s]), p0, None, gg, hp, "fp32")
+    del p, g, m, v
     torch.cuda.empty_cache()
