@@ -1,7 +1,9 @@
 """Parity at the largest shapes, against the fp64 oracle: 8192-sided
 matrices (the largest Muon matrices of the ragged workload) on the tiled
-engine, vectors at the longest side a plan accepts, and AdamW over the
-ragged workload's 1.17e9-element embedding and past 2^31 elements.
+engine, vectors at the longest side a plan accepts, AdamW over the
+ragged workload's 1.17e9-element embedding and past 2^31 elements, and the
+gradient-norm and state-statistics reductions past 2^31 elements (closed
+forms: constant buffers).
 
 The oracle cannot run NS on an 8192 x 8192 matrix in seconds, so the big
 matrices get an embedded input: the gradient is zero outside a scattered
@@ -189,4 +191,25 @@ def test_adamw_past_2_31_elements(gpu):
     for s, (p0, gg) in zip(samples, before):
         _adam_check(np64(p[s]), None, np64(m[s]), np64(v[s]), p0, None, gg, hp, "fp32")
     del p, g, m, v
+    torch.cuda.empty_cache()
+
+
+def test_guard_reductions_past_2_31_elements(gpu):
+    # closed forms past 2^31 elements: the global norm of a constant bf16
+    # buffer is c sqrt(n) (the fp64 sum of the c^2 is exact); the statistics
+    # of a constant fp32 buffer with one NaN and one +Inf beyond index 2^31
+    n = (1 << 31) + 7
+    g = torch.full((n,), 0.5, dtype=BF16, device=gpu)
+    st = M.read_clip_state(M.grad_norm_clip([g], 1.0))
+    assert abs(st["norm"] - 0.5 * n ** 0.5) <= 1e-7 * 0.5 * n ** 0.5
+    assert not st["skip"]
+    del g
+    x = torch.full((n,), 1.5, device=gpu)
+    x[(1 << 31) + 3] = float("nan")
+    x[(1 << 31) + 5] = float("inf")
+    s = M.read_state_stats(M.state_stats(x))
+    assert s["count"] == n - 2 and s["nonfinite"] == 2
+    assert s["mean"] == 1.5 and s["var"] == 0.0
+    assert s["min"] == s["max"] == s["absmax"] == 1.5
+    del x
     torch.cuda.empty_cache()
