@@ -501,7 +501,11 @@ hipError_t adamw_dispatch(void* params, float* master, const void* grads, void* 
                    (!MASTER || aligned(master, 32));
   const int64_t work = vec ? (n >> 3) : n;
   int64_t blocks = (work + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
+  // Up to 65536 blocks, one pass for groups of up to 1.3e8 elements.  A
+  // thread's next loads wait behind its stores (they may alias), so a
+  // grid-stride loop over few blocks keeps fewer bytes in flight: at 8192
+  // blocks a 6.6e7-element group ran 5% slower.
+  if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
   if (vec)
     hipLaunchKernelGGL((k_adamw_vec8<PT, GT, MT, VT, MASTER>),
