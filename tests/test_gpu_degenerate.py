@@ -88,8 +88,10 @@ def test_degenerate_gradients_match_closed_forms(gpu, ns_dtype, coef):
     grads = torch.zeros(n, device=gpu)
     mom = torch.zeros(n, device=gpu)
     out = torch.full((n,), 7.0, device=gpu)
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(12)
     for (o, r, c), (G, *_rest) in zip(mats, cases):
-        params[o:o + r * c] = torch.randn(r * c, device=gpu) * 0.02
+        params[o:o + r * c] = torch.randn(r * c, generator=gen, device=gpu) * 0.02
         grads[o:o + r * c] = torch.from_numpy(G.ravel()).to(gpu, torch.float32)
     plan = M.muon_plan_create(mats, n, "fp32", "fp32", ns_dtype)
     assert plan.info().small_mats == (3 if ns_dtype == "bf16" else 0)

@@ -134,8 +134,8 @@ def test_skipped_step_changes_nothing(gpu):
     am = _randn(n, torch.float32, gpu, 33)
     ag = _randn(n, torch.bfloat16, gpu, 34)
     ag[5] = float("inf")
-    m1 = torch.rand(n, device=gpu)
-    v1 = torch.rand(n, device=gpu)
+    m1 = _randn(n, torch.float32, gpu, 35)
+    v1 = _randn(n, torch.float32, gpu, 36).abs()
     clip = M.grad_norm_clip([s.grads, ag], 1.0)
     before = [t.clone() for t in (s.params, s.mom, s.out, ap, am, m1, v1)]
     M.muon_step(s.plan, s.params, s.grads, s.mom, s.ws, mhp(QUINTIC), s.out, clip=clip)

@@ -30,6 +30,12 @@ def np64(t):
     return t.detach().to(torch.float64).cpu().numpy()
 
 
+def _gen(dev, seed):
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return g
+
+
 def rel(a, b):
     nb = np.linalg.norm(b)
     return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
@@ -384,7 +390,7 @@ def test_stepwise_momentum_norm_and_iterates(gpu):
     for ns_dtype in ("fp32", "bf16"):
         mats, n = _flat([(96, 200), (200, 96)])
         s = Setup(mats, n, "fp32", "fp32", ns_dtype, gpu, seed=13)
-        s.mom[:] = torch.randn(n, device=gpu) * 0.1
+        s.mom[:] = torch.randn(n, generator=_gen(gpu, 131), device=gpu) * 0.1
         hp = mhp(QUINTIC)
         P0, G0, M0 = s.snapshot()
         M.muon_stage_momentum(s.plan, 0, s.grads, s.mom, s.ws, hp)
@@ -427,7 +433,7 @@ def test_muon_hyperparameter_variants(gpu, variant):
         hp = mhp((2.0, -1.5, 0.5), steps=3)
     elif variant == "no_nesterov":
         hp.nesterov = False
-        s.mom[:] = torch.randn(n, device=gpu) * 0.1
+        s.mom[:] = torch.randn(n, generator=_gen(gpu, 132), device=gpu) * 0.1
     elif variant == "mode1":
         hp.scale_mode = 1
     elif variant == "mode2":
