@@ -79,10 +79,12 @@ def test_captured_step_replays_bitwise(gpu, with_out):
     for t, s0 in zip(cap.tensors(), snapshot):
         t.copy_(s0)
     torch.cuda.synchronize()
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(99)
     for k in range(3):
         graph.replay()
         torch.cuda.synchronize()
-        junk = torch.randn(1 << 20, device=gpu).sum()  # eager work between replays
+        junk = torch.randn(1 << 20, generator=gen, device=gpu).sum()  # eager work between replays
         torch.cuda.synchronize()
         del junk
         for a, b in zip(cap.tensors(), ref[k]):
