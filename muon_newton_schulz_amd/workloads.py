@@ -152,6 +152,33 @@ def ragged_shapes(count: int = 500, seed: int = 5) -> List[Tuple[int, int]]:
     return out
 
 
+RAGGED_500_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                               "ragged_500_shapes.json")
+
+
+def frozen_ragged_shapes(path: str = RAGGED_500_JSON) -> List[Tuple[int, int]]:
+    """The ragged workload's shape list as committed (written once by
+    ``python -m muon_newton_schulz_amd.workloads --freeze-ragged`` from
+    ragged_shapes()), so that every run, test and profile sees the same
+    matrices whatever the NumPy version."""
+    with open(path) as f:
+        data = json.load(f)
+    return [(int(r), int(c)) for r, c in data["shapes"]]
+
+
+def write_frozen_ragged_shapes(path: str = RAGGED_500_JSON) -> None:
+    shapes = ragged_shapes()
+    data = {"recipe": "ragged_shapes(count=500, seed=5): NumPy PCG64 seeded with "
+                      "SeedSequence([5, 0]); per matrix i: d1, d2 = 64*U{8..128}; for i % 10 "
+                      "== 0 each dim + U{1..63}, clamped to 8192; i % 3 = 0 square (d1 x d1), "
+                      "1 tall (max x min), 2 wide (min x max)",
+            "count": len(shapes), "params": sum(r * c for r, c in shapes),
+            "shapes": [[r, c] for r, c in shapes]}
+    with open(path, "w") as f:
+        json.dump(data, f, separators=(",", ":"))
+        f.write("\n")
+
+
 def workload(name: str) -> Workload:
     mhp = MuonHParams()
     ahp = AdamWHParams()
@@ -180,7 +207,8 @@ def workload(name: str) -> Workload:
         adam = [AdamGroup("embedding", 163840 * 7168, "bf16", "bf16", True, 0.02, 0.02),
                 AdamGroup("vectors", 128 * 7168, "bf16", "bf16", True, 0.0, 0.02,
                           p_const=1.0)]
-        return Workload(name, 5, ragged_shapes(), "bf16", "bf16", 0.02, 0.02, adam, mhp, ahp)
+        return Workload(name, 5, frozen_ragged_shapes(), "bf16", "bf16", 0.02, 0.02, adam,
+                        mhp, ahp)
     raise KeyError(name)
 
 
@@ -347,3 +375,12 @@ def optimizer_state_bytes(n_params: int, optimizer: str) -> int:
     per = {"sgd": 0, "sgd_momentum": 4, "rmsprop": 4, "adam": 8, "adamw": 8,
            "adamw_8bit": 2, "muon": 4}[optimizer]
     return n_params * per
+
+
+if __name__ == "__main__":
+    import sys
+    if sys.argv[1:] == ["--freeze-ragged"]:
+        write_frozen_ragged_shapes()
+        print(f"wrote {RAGGED_500_JSON}")
+    else:
+        print("usage: python -m muon_newton_schulz_amd.workloads --freeze-ragged")
