@@ -3,12 +3,19 @@ on embedding, LM head and norm vectors) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--coef quintic|cubic]
 
+The default workload is the largest mixed one, ``ragged_500``: 500 ragged
+matrices (1.01e10 parameters) flattened into one buffer plus AdamW on a
+163840 x 7168 embedding and 128 vectors.
+
 Prints ONE JSON line.  The step is launched through the C ABI stage entry
 points (the same launches muon_step makes, in the same order, on torch's
 current stream) so that HIP events can bracket each kernel inside the
 timed region.  Inputs are seeded synthetic tensors already resident in
 HBM; gradients stay fixed across steps (the optimizer work does not
-depend on their values).
+depend on their values).  After the timed region the fp64 oracle checks
+sampled matrices and an AdamW slice of the first step and of the last
+timed step (their inputs are copied aside on the device before each of
+those steps: a few MB).
 """
 
 from __future__ import annotations
@@ -25,8 +32,15 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ns_gemm_dense_d2048_l16_traffic.md")
-MFMA_SUMMARY = os.path.join(ROOT, "profiles", "ns_gemm_dense_d2048_l16_mfma.md")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_summary(workload):
+    return os.path.join(PROFILES, f"ns_gemm_{workload}_traffic.md")
+
+
+def mfma_summary(workload):
+    return os.path.join(PROFILES, f"ns_gemm_{workload}_mfma.md")
 # the NS kernels are compiled from these two files
 NS_SOURCES = [os.path.join(ROOT, "muon_newton_schulz_amd", "csrc", f)
               for f in ("ns_gemm.hip", "muon_internal.h")]
@@ -47,7 +61,7 @@ def measured_traffic(workload):
     rocprofv3 counter summary, or None when the summary is missing, is for
     another workload, or was taken on a different kernel source."""
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(traffic_summary(workload)).read()
         block = text.split("```json", 1)[1].split("```", 1)[0]
         data = json.loads(block)
         sha = ns_source_sha256()
@@ -64,7 +78,7 @@ def measured_mfma_util(workload):
     it is missing, is for another workload, or was taken on a different
     kernel source."""
     try:
-        text = open(MFMA_SUMMARY).read()
+        text = open(mfma_summary(workload)).read()
         data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
         sha = ns_source_sha256()
     except (OSError, IndexError, ValueError):
@@ -74,13 +88,14 @@ def measured_mfma_util(workload):
     return {k: round(v["mfma_util_pct"], 1) for k, v in data["kernels"].items()}
 
 
-def mfma_ceiling():
-    """Sustained bf16 MFMA rate of this GPU (muon_newton_schulz_amd/mfma_ceiling:
-    back-to-back MFMAs from registers on every SIMD, no memory traffic), or
-    None if the program is missing or fails.  Run as a child process after
-    the timed region."""
+def run_ceiling(name):
+    """One of the stand-alone measurement programs (muon_newton_schulz_amd/
+    mfma_ceiling: back-to-back MFMAs from registers on every SIMD, no memory
+    traffic; hbm_ceiling: plain read + write, read and write streams over
+    2 GiB buffers), or None if it is missing or fails.  Run as a child
+    process after the timed region."""
     import subprocess
-    exe = os.path.join(ROOT, "muon_newton_schulz_amd", "mfma_ceiling")
+    exe = os.path.join(ROOT, "muon_newton_schulz_amd", name)
     if not os.path.exists(exe):
         return None
     try:
@@ -95,9 +110,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense_d2048_l16")
+    ap.add_argument("--workload", default="ragged_500")
     ap.add_argument("--coef", default="quintic", choices=["quintic", "cubic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-flops", type=float, default=5e12,
+                    help="fp64 NS flops of the oracle's CPU sample (about 10 s on 16 cores)")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle checks of the first and last step")
     ap.add_argument("--adamw-stream", choices=["same", "side"], default="side",
                     help="AdamW on the Muon stream, or on a second stream beside the NS kernels")
     ap.add_argument("--adamw-beside", type=int, choices=[1, 2, 3], default=1,
@@ -107,12 +126,52 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(wl, hp, sample_mats, adam_n):
-    """The fp64 oracle on a bounded sample of the same workload, timed on
-    the host cores.  Reported as NS TFLOP/s of the sample (same unit as
-    the GPU value) together with the wall time."""
+def van_der_corput(n):
+    """0, 1/2, 1/4, 3/4, 1/8, 5/8, 3/8, 7/8, ...: positions that spread any
+    prefix of the sequence evenly over [0, 1)."""
+    out = []
+    for k in range(n):
+        x, f, q = 0.0, 0.5, k
+        while q:
+            x += f * (q & 1)
+            q >>= 1
+            f /= 2
+        out.append(x)
+    return out
+
+
+def cpu_sample(wl, hp, flop_budget):
+    """Deterministic sample of the workload's matrices for the oracle: the
+    matrices sorted by NS flops, visited at van der Corput positions (so the
+    sample spreads over small and large matrices), each taken while the
+    sample's flops stay within the budget.  A workload within the budget is
+    taken whole."""
+    from muon_newton_schulz_amd import workloads as W
+    shapes = wl.shapes
+    fl = [W.ns_flops_matrix(r, c, hp.ns_steps, hp.ns_c) for r, c in shapes]
+    if sum(fl) <= flop_budget:
+        return list(range(len(shapes)))
+    order = sorted(range(len(shapes)), key=lambda i: (fl[i], i))
+    picked, seen, total = [], set(), 0
+    for x in van_der_corput(4 * len(order)):
+        j = order[min(len(order) - 1, int(x * len(order)))]
+        if j in seen:
+            continue
+        seen.add(j)
+        if total + fl[j] <= flop_budget:
+            picked.append(j)
+            total += fl[j]
+    return sorted(picked)
+
+
+def cpu_baseline(wl, hp, flop_budget, adam_n):
+    """The fp64 oracle, as it stands, on a bounded sample of the same
+    workload, timed on the host cores: the full Muon step of the sampled
+    matrices (cpu_sample) and AdamW over adam_n elements.  The whole-step
+    oracle time is extrapolated linearly (Muon by NS flops, AdamW by
+    elements) and reported in the GPU value's unit: NS flops of the whole
+    step per second of the whole step."""
     import numpy as np
-    import torch
     from threadpoolctl import threadpool_info
 
     from muon_newton_schulz_amd import workloads as W
@@ -123,43 +182,128 @@ def cpu_baseline(wl, hp, sample_mats, adam_n):
                    ns_steps=hp.ns_steps, eps=hp.eps, scale_mode=hp.scale_mode,
                    rms_target=hp.rms_target)
     mats = wl.mats()
-    inputs = []
-    for i in sample_mats:
+    sample = cpu_sample(wl, hp, flop_budget)
+    t_muon = 0.0
+    for i in sample:   # inputs drawn per matrix (not timed), then its oracle step
         o, r, c = mats[i]
         w = W.normal_tensor(r * c, wl.w_std, wl.param_dtype, W.seed_key(wl.config_id, 0, i, 0))
         g = W.normal_tensor(r * c, wl.g_std, wl.grad_dtype, W.seed_key(wl.config_id, 1, i, 1))
-        inputs.append((w.double().numpy().reshape(r, c), g.double().numpy().reshape(r, c),
-                       np.zeros((r, c))))
-    grp = wl.adam[0]
-    ap = W.normal_tensor(adam_n, grp.p_std, "fp32", 99).double().numpy()
-    ag = W.normal_tensor(adam_n, grp.g_std, grp.grad_dtype, 98).double().numpy()
-    ahp = O.AdamWHP(wl.adam_hp.lr, wl.adam_hp.beta1, wl.adam_hp.beta2, wl.adam_hp.eps,
-                    wl.adam_hp.weight_decay)
-    t0 = time.perf_counter()
-    for (w, g, m) in inputs:
-        O.muon_matrix_math(w, g, m, ohp)
-    t1 = time.perf_counter()
-    O.adamw_step_stored(O.bf16_round(ap), ap, ag, np.zeros(adam_n), np.zeros(adam_n), ahp, 1,
-                        "bf16")
-    t2 = time.perf_counter()
-    flops = sum(W.ns_flops_matrix(mats[i][1], mats[i][2], hp.ns_steps, hp.ns_c)
-                for i in sample_mats)
+        w, g = w.double().numpy().reshape(r, c), g.double().numpy().reshape(r, c)
+        t0 = time.perf_counter()
+        O.muon_matrix_math(w, g, np.zeros((r, c)), ohp)
+        t_muon += time.perf_counter() - t0
+    n_adam_total = wl.adam_numel()
+    adam_n = min(adam_n, n_adam_total)
+    t_adam = 0.0
+    if adam_n:
+        grp = wl.adam[0]
+        ap = W.normal_tensor(adam_n, max(grp.p_std, 0.02), "fp32", 99).double().numpy()
+        ag = W.normal_tensor(adam_n, grp.g_std, grp.grad_dtype, 98).double().numpy()
+        ahp = O.AdamWHP(wl.adam_hp.lr, wl.adam_hp.beta1, wl.adam_hp.beta2, wl.adam_hp.eps,
+                        wl.adam_hp.weight_decay)
+        t0 = time.perf_counter()
+        O.adamw_step_stored(O.bf16_round(ap), ap, ag, np.zeros(adam_n), np.zeros(adam_n), ahp,
+                            1, "bf16")
+        t_adam = time.perf_counter() - t0
+    flops_sample = sum(W.ns_flops_matrix(mats[i][1], mats[i][2], hp.ns_steps, hp.ns_c)
+                       for i in sample)
+    flops_total = W.ns_flops_workload(wl, hp.ns_steps, hp.ns_c)
+    full = len(sample) == len(mats) and adam_n == n_adam_total
+    t_step = (t_muon * flops_total / flops_sample
+              + (t_adam * n_adam_total / adam_n if adam_n else 0.0))
     threads = max((d.get("num_threads", 1) for d in threadpool_info()
                    if d.get("user_api") == "blas"), default=1)
-    sample_params = sum(mats[i][1] * mats[i][2] for i in sample_mats)
+    sample_params = sum(mats[i][1] * mats[i][2] for i in sample)
     return {
-        "value": flops / (t1 - t0) / 1e12,
+        "value": flops_total / t_step / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle: full Muon step on {len(sample_mats)} of "
-                   f"{len(mats)} matrices ({sample_params / wl.muon_numel():.1%} of the Muon "
-                   f"params, {flops / 1e12:.2f} TFLOP of NS) in {t1 - t0:.1f} s, plus AdamW on "
-                   f"{adam_n} elements in {t2 - t1:.2f} s "
-                   f"({adam_n * 28 / (t2 - t1) / 1e9:.2f} GB/s algorithmic)"),
-        "muon_seconds": t1 - t0,
-        "adamw_seconds": t2 - t1,
+        "sample": (f"fp64 NumPy oracle, {'whole step' if full else 'extrapolated'}: full Muon "
+                   f"step on {len(sample)} of {len(mats)} matrices ({sample_params / wl.muon_numel():.1%}"
+                   f" of the Muon params, {flops_sample / 1e12:.2f} of {flops_total / 1e12:.1f} "
+                   f"TFLOP of NS; matrices sorted by flops, taken at van der Corput positions "
+                   f"within a {flop_budget / 1e12:.3g} TFLOP budget) in {t_muon:.1f} s, plus "
+                   f"AdamW on {adam_n} of {n_adam_total} elements in {t_adam:.2f} s; whole "
+                   f"step {t_step:.0f} s {'measured' if full else 'extrapolated linearly by NS flops and AdamW elements'}"),
+        "extrapolated": not full,
+        "sample_matrices": sample,
+        "ns_tflops_sample": flops_sample / t_muon / 1e12 if t_muon else None,
+        "muon_seconds": t_muon,
+        "adamw_seconds": t_adam,
+        "step_seconds_extrapolated": t_step,
     }
+
+
+def parity_matrices(wl):
+    """Matrices the oracle checks at the first and last step: the smallest
+    whose offset and cols are multiples of 8 (the update fused into the last
+    NS phase, with bf16 parameters) and the smallest of the others (the
+    separate apply kernel)."""
+    mats = wl.mats()
+    size = lambda i: mats[i][1] * mats[i][2]  # noqa: E731
+    on8 = [i for i, (o, r, c) in enumerate(mats) if o % 8 == 0 and c % 8 == 0]
+    off8 = [i for i, (o, r, c) in enumerate(mats) if not (o % 8 == 0 and c % 8 == 0)]
+    return sorted({min(grp, key=size) for grp in (on8, off8) if grp})
+
+
+def half_ulp(x, dtype):
+    """Half an ulp of each stored value (bf16: 8 significant bits, fp32: 24)."""
+    import numpy as np
+    bits = 8 if dtype == "bf16" else 24
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - bits)
+
+
+def oracle_check(wl, hp, ahp_w, snap_pre, snap_post, t):
+    """fp64 oracle against one step's results: per sampled matrix M (<= 2e-6)
+    and the update W implies, O_impl = (decay W0 - W1) / step, against O
+    (<= 1e-2 bf16 NS, 1e-4 fp32 NS, plus the storage rounding of W1 over
+    step); AdamW master, m, v (<= 2e-6) and the 16-bit parameter equal to
+    the cast of the master."""
+    import math
+
+    import numpy as np
+
+    from oracle import muon_oracle as O
+    ohp = O.MuonHP(lr=hp.lr, weight_decay=hp.weight_decay, momentum=hp.momentum,
+                   nesterov=hp.nesterov, ns_a=hp.ns_a, ns_b=hp.ns_b, ns_c=hp.ns_c,
+                   ns_steps=hp.ns_steps, eps=hp.eps, scale_mode=hp.scale_mode,
+                   rms_target=hp.rms_target)
+
+    def rel(a, b):
+        nb = np.linalg.norm(b)
+        return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+    tol_o = 1e-2
+    res, ok = {"t": t, "matrices": {}}, True
+    for i, (r, c, W0, G, M0) in snap_pre["mats"].items():
+        W1, M1 = snap_post["mats"][i][2], snap_post["mats"][i][4]
+        _, Mr, Or = O.muon_matrix_math(W0, G, M0, ohp)
+        em = rel(M1, O.fp32_round(Mr))
+        decay = float(np.float32(1.0) - np.float32(hp.lr) * np.float32(hp.weight_decay))
+        step = float(np.float32(hp.lr) * np.float32(
+            O.update_scale(r, c, hp.scale_mode, hp.rms_target)))
+        eo = rel((decay * W0 - W1) / step, Or)
+        slack = float(np.linalg.norm(half_ulp(W1, wl.param_dtype)) / (step * np.linalg.norm(Or)))
+        good = em <= 2e-6 and eo <= tol_o + slack
+        ok &= good
+        res["matrices"][str(i)] = {"shape": [r, c], "M": em, "O_from_W": eo,
+                                   "O_tol": tol_o + slack, "ok": good}
+    if snap_pre.get("adam") is not None:
+        p0, m0, e0, v0, g = snap_pre["adam"]
+        p1, m1, e1, v1, _ = snap_post["adam"]
+        pdt = wl.adam[0].param_dtype
+        pr, mr, er, vr = O.adamw_step_stored(p0, m0, g, e0, v0, ahp_w, t, pdt)
+        th1 = m1 if m1 is not None else p1
+        thr = mr if mr is not None else pr
+        ea = {"theta": rel(th1, thr), "m": rel(e1, er), "v": rel(v1, vr)}
+        cast_ok = True if m1 is None else bool(np.array_equal(p1, O.round_to(m1, pdt)))
+        good = max(ea.values()) <= 2e-6 and cast_ok
+        ok &= good
+        res["adamw"] = {**ea, "param_is_cast_of_master": cast_ok, "ok": good}
+    res["ok"] = bool(ok)
+    return res
 
 
 def main():
@@ -251,24 +395,89 @@ def main():
             stream.wait_stream(side)
         return marks
 
+    # ---- oracle checks of the first step and of the last timed step: the
+    # inputs and results of a few sampled matrices and of an AdamW slice are
+    # copied aside on the device (device-to-device, on the stream: a few MB)
+    do_parity = not args.no_parity
+    chk = parity_matrices(wl) if do_parity else []
+    mats = wl.mats()
+    asl = slice(0, min(4096, wl.adam[0].numel)) if wl.adam else None
+
+    def snap():
+        out = {"mats": {}, "adam": None}
+        for i in chk:
+            o, r, c = mats[i]
+            sl = slice(o, o + r * c)
+            out["mats"][i] = (r, c, inp.params[sl].clone(), inp.grads[sl].clone(),
+                              inp.momentum[sl].clone())
+        if asl is not None:
+            a = adam[0]
+            out["adam"] = (a.param[asl].clone(),
+                           a.master[asl].clone() if a.master is not None else None,
+                           a.exp_avg[asl].clone(), a.exp_avg_sq[asl].clone(), a.grad[asl].clone())
+        return out
+
+    def host(sn):
+        f64 = lambda t: None if t is None else t.double().cpu().numpy()  # noqa: E731
+        return {"mats": {i: (r, c, f64(w).reshape(r, c), f64(g).reshape(r, c),
+                             f64(m).reshape(r, c))
+                         for i, (r, c, w, g, m) in sn["mats"].items()},
+                "adam": None if sn["adam"] is None else tuple(f64(t) for t in sn["adam"])}
+
+    snaps = {}
+    n_done = 0
+
+    def counted_step(record):
+        nonlocal n_done
+        if do_parity and n_done == 0:
+            snaps["first_pre"] = snap()
+        marks = one_step(record)
+        n_done += 1
+        if do_parity and n_done == 1:
+            snaps["first_post"] = snap()
+        return marks
+
     for _ in range(args.warmup):
-        one_step(False)
+        counted_step(False)
     if calib is not None:
         calib[1].copy_(calib[0])
     torch.cuda.synchronize()
 
     start, end = ev(), ev()
+    step_ev = [ev() for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     all_marks = []
-    for _ in range(args.steps):
-        all_marks.append(one_step(True))
+    for j in range(args.steps):
+        if do_parity and j == args.steps - 1:
+            snaps["last_pre"] = snap()
+        step_ev[j].record(stream)
+        all_marks.append(counted_step(True))
+    step_ev[args.steps].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
+    step_ms = sorted(step_ev[j].elapsed_time(step_ev[j + 1]) for j in range(args.steps))
+    ms_median = (step_ms[(args.steps - 1) // 2] + step_ms[args.steps // 2]) / 2
+    parity = None
+    if do_parity:
+        snaps["last_post"] = snap()
+        torch.cuda.synchronize()
+        ahp_o = None
+        if wl.adam:
+            from oracle import muon_oracle as O
+            ahp_o = O.AdamWHP(ahp.lr, ahp.beta1, ahp.beta2, ahp.eps, ahp.weight_decay)
+        parity = {
+            "first_step": oracle_check(wl, hp, ahp_o, host(snaps["first_pre"]),
+                                       host(snaps["first_post"]), 1),
+            "last_step": oracle_check(wl, hp, ahp_o, host(snaps["last_pre"]),
+                                      host(snaps["last_post"]), n_done),
+        }
+        parity["ok"] = parity["first_step"]["ok"] and parity["last_step"]["ok"]
+        del snaps
 
     def avg_ms(key):
         vals = [a.elapsed_time(b) for mk in all_marks for (a, b) in mk[key]]
@@ -407,7 +616,8 @@ def main():
                      "max_logit_per_head_all_clipped": entry(per_head, 2)}
         del fplan, hplan
 
-    ceiling = mfma_ceiling()
+    ceiling = run_ceiling("mfma_ceiling")
+    hbm_ceiling = run_ceiling("hbm_ceiling")
 
     # ---- algorithmic work
     shapes = wl.shapes
@@ -436,6 +646,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": ms_median,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -498,8 +709,14 @@ def main():
                             if adamw_alone_ms else None),
             "peak": PEAK_HBM_GBPS,
             "plain_copy_1GiB": copy_gbps,
+            # best plain copy / read / write streams of this GPU over 2 GiB
+            # buffers (hbm_ceiling), measured after the timed region
+            "stream_ceiling": hbm_ceiling,
         },
         "wall_s_timed_region": wall1 - wall0,
+        # fp64 oracle on sampled matrices and an AdamW slice of the first step
+        # and of the last timed step
+        "parity": parity,
         # optimizer-tutorial 5.4 safety net, timed separately from the step
         # (algorithmic bytes: every gradient, or the momentum, read once)
         "guard": guard,
@@ -510,9 +727,7 @@ def main():
         "muon_clip": muon_clip,
     }
     if not args.no_cpu_baseline:
-        # the first three layers of the stack: 12 square + 9 rectangular matrices
-        sample = list(range(min(21, len(shapes))))
-        result["cpu_baseline"] = cpu_baseline(wl, hp, sample, 1 << 23)
+        result["cpu_baseline"] = cpu_baseline(wl, hp, args.cpu_flops, 1 << 23)
     print(json.dumps(result), flush=True)
 
 

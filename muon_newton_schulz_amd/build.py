@@ -14,9 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmuon.so")
 SOURCES = ["muon_abi.hip", "elementwise.hip", "ns_gemm.hip", "ns_small.hip", "guard.hip", "clip.hip"]
-# stand-alone measurement program: the GPU's sustained bf16 MFMA rate
-CEILING = os.path.join(PKG, "mfma_ceiling")
-CEILING_SRC = "mfma_ceiling.hip"
+# stand-alone measurement programs: the GPU's sustained bf16 MFMA rate and
+# its HBM stream rates
+PROGRAMS = [("mfma_ceiling", "mfma_ceiling.hip"), ("hbm_ceiling", "hbm_ceiling.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -54,7 +54,8 @@ def build(verbose: bool = True) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     _hipcc([HIPCC, *FLAGS, *srcs], LIB, verbose)
     exe_flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
-    _hipcc([HIPCC, *exe_flags, os.path.join(CSRC, CEILING_SRC)], CEILING, verbose)
+    for exe, src in PROGRAMS:
+        _hipcc([HIPCC, *exe_flags, os.path.join(CSRC, src)], os.path.join(PKG, exe), verbose)
     return LIB
 
 
