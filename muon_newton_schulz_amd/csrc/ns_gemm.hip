@@ -232,6 +232,11 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // MFMA m = 4 bj + bi runs iff bit m is set
   constexpr uint32_t MASK = ROLE == 0 ? 0xFFFFu : ROLE == 1 ? 0xF731u : 0x00FFu;
   static_assert(ROLE <= 2 || (ROLE == 3 ? PHASE == 3 : true), "half-height tiles are phase 3's");
+  // A guarded step that is skipped leaves W untouched: a matrix whose
+  // update this tile would apply needs none of the tile's work (it writes
+  // no X').  The flag is uniform over the workgroup.
+  if constexpr (APPLY)
+    if (md.fuse && g.clip != nullptr && g.clip->skip) return;
   uint16_t* ws = static_cast<uint16_t*>(g.ws);
 
   // operands
@@ -469,7 +474,6 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   uint16_t* Wm = nullptr;
   if constexpr (APPLY) {
     if (md.fuse) {
-      if (g.clip != nullptr && g.clip->skip) return;  // guarded step: W untouched
       to_w = true;
       ak = apply_consts(md.rows, md.cols, g.lr, g.wd, g.scale_mode, g.rms_target);
       Wm = g.params + md.off;
