@@ -36,10 +36,12 @@
  *   - Buffers passed to one call must not alias each other.
  *   - Non-finite inputs propagate into the outputs unless the step is
  *     guarded through a clip state (grad_norm_clip below).
- *   - Muon normalises U inside its first products, which accumulate the
- *     unnormalised U U^T in fp32: a step is in range while
- *     n * max|u|^2 < 3.4e38 (n the long side; |u| below about 1e17 for
- *     n <= 1e4).
+ *   - Muon folds the normalisation X0 = U / (||U||_F + eps) into its first
+ *     products, which accumulate the unnormalised U U^T in fp32.  A matrix
+ *     whose ||U||_F (finite, nonzero) lies outside [2^-40, 2^40] first has
+ *     its U scaled by an exact power of two, so every step is in range for
+ *     any finite fp32 U with ||U||_F below the fp32 maximum.  With eps = 0
+ *     an all-zero U gives 0/0, which propagates as NaN.
  */
 #ifndef MUON_H_
 #define MUON_H_
@@ -250,7 +252,8 @@ int muon_stage_ns_apply(const muon_plan_t* plan, int32_t wave, void* params, voi
 
 /* Copy the current NS iterate of every matrix of a wave into a flat fp32
  * buffer at each matrix's elements, in the caller's [rows, cols] layout
- * (after muon_stage_momentum it is U, the un-normalised NS input).
+ * (after muon_stage_momentum it is U, the un-normalised NS input, or
+ * U * 2^k for a matrix whose ||U||_F lies outside [2^-40, 2^40]).
  * For stepwise checks. */
 int muon_stage_export_x(const muon_plan_t* plan, int32_t wave, const void* workspace,
                         size_t workspace_bytes, int32_t iter_done, float* out,

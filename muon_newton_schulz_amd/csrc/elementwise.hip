@@ -7,7 +7,8 @@
 //                   per 64x64 tile.
 //  k_norm_finalize  per-matrix ||U||_F and 1/(||U||_F + eps) (Zhihu answer
 //                   on K2, section 4: the Frobenius norm bounds the
-//                   spectral norm).
+//                   spectral norm); rescales X0 by a power of two for a
+//                   norm outside the folded normalisation's range.
 //  k_apply          W <- (1 - lr*wd) W - lr*s*O (optimizer tutorial,
 //                   section 3.1, decoupled decay; scale s per the K2
 //                   answer, sections 3.1 / 3.2).
@@ -229,11 +230,58 @@ __device__ __forceinline__ f32x16_t load_nat_tile(const MatDev& md, const UT* X,
   return o;
 }
 
+// The first NS products accumulate the unnormalised U U^T in fp32 and
+// scale it by inv^2 in the epilogue.  That is exact in range while
+// ||U||_F lies in [2^-40, 2^40]: products of the entries that carry the
+// norm stay normal fp32 numbers, and neither U U^T nor inv^2 can exceed
+// 2^80.  A matrix whose norm lies outside (finite and nonzero) has its
+// iterate X0 = U scaled in place by 2^k, with ||U||_F * 2^k in [0.5, 1),
+// and inv divided by 2^k, so that inv * X0 is unchanged and every product
+// is in range.  Scaling by a power of two is exact (bf16 and fp32 alike).
+// Returns k (0 inside the range).
+__device__ __forceinline__ int norm_rescale_exp(double nrm) {
+  if (!(nrm > 0.0) || !(nrm < HUGE_VAL) || (nrm >= 0x1p-40 && nrm <= 0x1p40)) return 0;
+  int e;
+  (void)frexp(nrm, &e);  // nrm = f * 2^e, f in [0.5, 1)
+  return -e;
+}
+
+template <typename UT>
+__device__ __forceinline__ void scale_pow2(UT* x, int64_t n, int k);
+template <>
+__device__ __forceinline__ void scale_pow2<float>(float* x, int64_t n, int k) {
+  for (int64_t i = threadIdx.x; i < n / 4; i += blockDim.x) {
+    float4 v = reinterpret_cast<float4*>(x)[i];
+    v.x = ldexpf(v.x, k); v.y = ldexpf(v.y, k); v.z = ldexpf(v.z, k); v.w = ldexpf(v.w, k);
+    reinterpret_cast<float4*>(x)[i] = v;
+  }
+}
+template <>
+__device__ __forceinline__ void scale_pow2<uint16_t>(uint16_t* x, int64_t n, int k) {
+  for (int64_t i = threadIdx.x; i < n / 8; i += blockDim.x) {
+    uint4 v = reinterpret_cast<uint4*>(x)[i];
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = ldexpf(__uint_as_float(w[e] << 16), k);
+      const float hi = ldexpf(__uint_as_float(w[e] & 0xffff0000u), k);
+      w[e] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    }
+    reinterpret_cast<uint4*>(x)[i] = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// One block per matrix: ||U||_F from the fixed-order partials, inv =
+// 1/(||U||_F + eps), and the power-of-two rescale of X0 for a norm out of
+// the folded normalisation's range (the rare path: the whole block scales
+// the matrix's iterate).
+template <typename UT>
 __global__ __launch_bounds__(256) void k_norm_finalize(const MatDev* __restrict__ mats,
                                                        int mat_begin,
                                                        const double* __restrict__ partials,
                                                        float* __restrict__ norms,
-                                                       float* __restrict__ inv, float eps) {
+                                                       float* __restrict__ inv, float eps,
+                                                       UT* __restrict__ ws) {
   __shared__ double red[256];
   const MatDev md = mats[mat_begin + blockIdx.x];
   double s = 0.0;
@@ -245,11 +293,14 @@ __global__ __launch_bounds__(256) void k_norm_finalize(const MatDev* __restrict_
     if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
+  const double nrm = sqrt(red[0]);
+  const int k = norm_rescale_exp(nrm);
   if (threadIdx.x == 0) {
-    const double nrm = sqrt(red[0]);
     norms[md.widx] = static_cast<float>(nrm);
-    inv[md.widx] = static_cast<float>(1.0 / (nrm + static_cast<double>(eps)));
+    inv[md.widx] = static_cast<float>(ldexp(1.0 / (nrm + static_cast<double>(eps)), -k));
   }
+  if (k != 0)
+    scale_pow2<UT>(ws + md.ws_x[0], static_cast<int64_t>(md.m_pad) * md.n_pad, k);
 }
 
 template <typename PT, typename UT>
@@ -562,10 +613,14 @@ hipError_t launch_momentum(const MatDev* mats, const Item* items, int n_items, i
 
 hipError_t launch_norm_finalize(const MatDev* mats, int mat_begin, int n_mats,
                                 const double* partials, float* norms, float* inv, float eps,
-                                hipStream_t s) {
+                                int ns_dtype, void* ws, hipStream_t s) {
   if (n_mats == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_norm_finalize, dim3(n_mats), dim3(256), 0, s, mats, mat_begin, partials,
-                     norms, inv, eps);
+  if (ns_dtype == 1)
+    hipLaunchKernelGGL(k_norm_finalize<uint16_t>, dim3(n_mats), dim3(256), 0, s, mats, mat_begin,
+                       partials, norms, inv, eps, static_cast<uint16_t*>(ws));
+  else
+    hipLaunchKernelGGL(k_norm_finalize<float>, dim3(n_mats), dim3(256), 0, s, mats, mat_begin,
+                       partials, norms, inv, eps, static_cast<float*>(ws));
   return hipGetLastError();
 }
 

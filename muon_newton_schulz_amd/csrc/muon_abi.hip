@@ -553,7 +553,7 @@ int muon_stage_momentum(const muon_plan_t* plan, int32_t wave, const void* grads
   e = muon::launch_norm_finalize(plan->d_mats, w.mat_begin, w.mat_end - w.mat_begin, partials,
                                  reinterpret_cast<float*>(ws_bytes_ptr(workspace, w.norm_off)),
                                  reinterpret_cast<float*>(ws_bytes_ptr(workspace, w.inv_off)),
-                                 hp->eps, stream);
+                                 hp->eps, plan->ns_dtype, workspace, stream);
   if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
   return MUON_OK;
 }

@@ -99,9 +99,11 @@ hipError_t launch_momentum(const MatDev* mats, const Item* items, int n_items,
                            int grad_dtype, int ns_dtype, const void* grads, float* mom,
                            void* ws, double* partials, float mu, int nesterov,
                            const ClipState* clip, hipStream_t s);
+// Also rescales X0 (in the workspace ws, NS dtype ns_dtype) by a power of
+// two, folded into inv, for a matrix whose norm lies outside [2^-40, 2^40].
 hipError_t launch_norm_finalize(const MatDev* mats, int mat_begin, int n_mats,
                                 const double* partials, float* norms, float* inv,
-                                float eps, hipStream_t s);
+                                float eps, int ns_dtype, void* ws, hipStream_t s);
 hipError_t launch_apply(const MatDev* mats, const Item* items, int n_items, int param_dtype,
                         int ns_dtype, void* params, const void* ws, const float* inv,
                         float o_scale_by_inv, int x_final, float lr, float wd,

@@ -541,15 +541,21 @@ def test_ragged_shapes_full_size_sampled(gpu):
     _workload_sampled(gpu, "ragged_500", sample, mhp(QUINTIC), first=40)
 
 
-@pytest.mark.parametrize("g_std", [1e14, 1e-25])
-def test_extreme_gradient_scales_normalise_like_the_oracle(gpu, g_std):
-    # |u| ~ 1e13: n max|u|^2 ~ 1e29, inside the fp32 range that the first
-    # products (which see the unnormalised U) need; |u| ~ 1e-26: u^2
-    # underflows fp32, and ||U||_F then sits far below eps on both sides.
-    # Tiled and fused small-matrix paths, both NS dtypes.
+@pytest.mark.parametrize("g_std,eps", [(1e14, 1e-7), (1e-25, 1e-7), (1e18, 1e-7), (1e-22, 0.0)])
+def test_extreme_gradient_scales_normalise_like_the_oracle(gpu, g_std, eps):
+    # ||U||_F outside [2^-40, 2^40]: the norm kernel scales U by a power of
+    # two (folded into inv) before the first products, which otherwise
+    # accumulate U U^T unnormalised in fp32.  |u| ~ 1e17: U U^T and inv^2
+    # would leave the fp32 range; |u| ~ 1e-23 with eps = 0: inv^2 would
+    # overflow and u^2 underflow; |u| ~ 1e-26 with eps = 1e-7: ||U||_F sits
+    # far below eps.  Tiled and fused small-matrix paths, both NS dtypes.
     mats, n = _flat([(300, 520), (520, 300), (96, 200), (64, 64)])
     for nsd, pdt in (("bf16", "bf16"), ("fp32", "fp32")):
         s = Setup(mats, n, pdt, pdt, nsd, gpu, seed=17, w_std=0.02, g_std=g_std)
-        worst = check_muon_step(s, mhp(QUINTIC))
+        worst = check_muon_step(s, mhp(QUINTIC, eps=eps))
         assert np.isfinite(np64(s.out)).all() and np.isfinite(np64(s.params)).all()
         assert worst["O"] <= TOL_O[nsd]
+        norms = torch.zeros(len(mats), device=gpu)
+        M.muon_stage_export_norms(s.plan, 0, s.ws, norms)
+        torch.cuda.synchronize()
+        assert np.isfinite(np64(norms)).all() and (np64(norms) > 0).all()
