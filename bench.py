@@ -117,6 +117,8 @@ def parse():
                     help="fp64 NS flops of the oracle's CPU sample (about 10 s on 16 cores)")
     ap.add_argument("--no-parity", action="store_true",
                     help="skip the oracle checks of the first and last step")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the MFMA and HBM ceiling programs (profiling runs)")
     ap.add_argument("--adamw-stream", choices=["same", "side"], default="side",
                     help="AdamW on the Muon stream, or on a second stream beside the NS kernels")
     ap.add_argument("--adamw-beside", type=int, choices=[1, 2, 3], default=1,
@@ -616,8 +618,8 @@ def main():
                      "max_logit_per_head_all_clipped": entry(per_head, 2)}
         del fplan, hplan
 
-    ceiling = run_ceiling("mfma_ceiling")
-    hbm_ceiling = run_ceiling("hbm_ceiling")
+    ceiling = None if args.no_ceilings else run_ceiling("mfma_ceiling")
+    hbm_ceiling = None if args.no_ceilings else run_ceiling("hbm_ceiling")
 
     # ---- algorithmic work
     shapes = wl.shapes

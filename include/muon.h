@@ -28,8 +28,11 @@
  *     muon_last_error() gives a message for the last failure on the
  *     calling thread.
  *   - Device pointers are plain HIP device addresses on the device that was
- *     current when the plan was created.  All of them are owned by the
- *     caller; the library keeps no pointer after a call returns.
+ *     current when the plan was uploaded.  All device memory is owned by
+ *     the caller; the library allocates none.  The only device pointer it
+ *     keeps after a call returns is a plan's table buffer (muon_plan_upload,
+ *     muon_clip_plan_upload), which the caller keeps alive while the plan
+ *     is used.
  *   - Work is enqueued on the caller's HIP stream; the library never
  *     synchronises.  A kernel fault surfaces at the caller's next
  *     synchronisation of that stream.
@@ -136,9 +139,11 @@ typedef struct {
 
 /* Opaque plan: matrix descriptors validated, orientation (tall matrices
  * are iterated transposed so the Gram matrix is min(r,c) square), padding
- * to the GEMM tile, workspace layout, tile lists and waves.  Immutable
- * after creation; the plan owns one small device allocation holding its
- * tables, freed by muon_plan_destroy. */
+ * to the GEMM tile, workspace layout, tile lists and waves ([K2] 2.2: the
+ * flat concatenation, each matrix whole at its offset).  Creation is
+ * host-only.  Its tables go to the device once, into a caller buffer, with
+ * muon_plan_upload; after that the plan is read-only and steps on several
+ * streams may share it. */
 typedef struct muon_plan muon_plan_t;
 
 typedef struct {
@@ -167,9 +172,10 @@ int muon_workspace_size(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_
                         int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
                         size_t workspace_cap, size_t* workspace_bytes);
 
-/* Build a plan on the current device.  n_mats may be 0 (steps are then
- * no-ops).  On success *out owns the plan and *workspace_bytes is the
- * size of the device workspace every step needs. */
+/* Build a plan (host memory only; no HIP call, no device memory).  n_mats
+ * may be 0 (steps are then no-ops).  On success *out owns the plan and
+ * *workspace_bytes is the size of the device workspace every step needs.
+ * Upload the plan (muon_plan_upload) before its first step. */
 int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                      int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
                      size_t workspace_cap, muon_plan_t** out, size_t* workspace_bytes);
@@ -196,7 +202,27 @@ int muon_plan_create_ex(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_
                         size_t workspace_cap, uint32_t flags, muon_plan_t** out,
                         size_t* workspace_bytes);
 
+/* Frees the plan's host memory (the caller frees its table buffer). */
 void muon_plan_destroy(muon_plan_t* plan);
+
+/* Bytes of device memory the plan's tables take (matrix descriptors, the
+ * elementwise and GEMM tile lists); 0 for a plan without matrices.
+ * Host-only. */
+size_t muon_plan_table_bytes(const muon_plan_t* plan);
+
+/* Copies the plan's tables into `tables` with one hipMemcpyAsync on
+ * `stream` and binds the plan to the current device.
+ *   tables      : device memory on the current device, owned by the caller,
+ *                 >= muon_plan_table_bytes(plan) bytes, 256-byte aligned
+ *                 (may be NULL when that size is 0).  The caller keeps it
+ *                 alive and unmodified while the plan is used; the copy
+ *                 reads the plan's host memory, so the plan must outlive it.
+ *   table_bytes : size of `tables`
+ * Steps on `stream` are ordered after the copy; steps on other streams must
+ * be ordered after it by the caller.  Every step needs an uploaded plan
+ * (MUON_ERR_INVALID_ARG otherwise) on the device it was uploaded on.
+ * Uploading again (e.g. to another buffer) must not overlap running steps. */
+int muon_plan_upload(muon_plan_t* plan, void* tables, size_t table_bytes, hipStream_t stream);
 
 int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info);
 
@@ -364,14 +390,24 @@ typedef struct muon_clip_plan muon_clip_plan_t;
 
 /* Validates the blocks (inside [0, flat_numel), rows and cols >= 1,
  * rows * cols < 2^31, no element in two blocks, group in [0, max(n_groups,
- * 1))), splits them into fixed chunks and uploads the tables to the
- * current device (the only device memory the library allocates; freed by
- * muon_clip_plan_destroy).  *workspace_bytes: device workspace muon_clip
- * needs in Frobenius mode (0 in max-logit mode).  targets is a host array. */
+ * 1))) and splits them into fixed chunks, in host memory (no HIP call).
+ * *workspace_bytes: device workspace muon_clip needs in Frobenius mode (0
+ * in max-logit mode).  targets is a host array.  Upload the plan
+ * (muon_clip_plan_upload) before its first use. */
 int muon_clip_plan_create(const muon_clip_target_t* targets, int32_t n_targets,
                           int64_t flat_numel, int32_t param_dtype, int32_t n_groups,
                           muon_clip_plan_t** out, size_t* workspace_bytes);
+/* Frees the plan's host memory (the caller frees its table buffer). */
 void muon_clip_plan_destroy(muon_clip_plan_t* plan);
+/* Bytes of device memory of the plan's block and chunk tables (0 without
+ * blocks).  Host-only. */
+size_t muon_clip_plan_table_bytes(const muon_clip_plan_t* plan);
+/* Copies the tables into `tables` (caller-owned device memory on the
+ * current device, >= muon_clip_plan_table_bytes bytes, 256-byte aligned,
+ * kept alive and unmodified while the plan is used) with one
+ * hipMemcpyAsync on `stream`, as muon_plan_upload does for a Muon plan. */
+int muon_clip_plan_upload(muon_clip_plan_t* plan, void* tables, size_t table_bytes,
+                          hipStream_t stream);
 
 /* MuonClip on params (device, the plan's dtype, bf16 or fp32), in place,
  * after the optimizer step ([K2] 4):

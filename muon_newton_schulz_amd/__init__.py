@@ -32,14 +32,16 @@ MUON_DTYPE_FP16 = 2
 
 EXPORTED = [
     "muon_workspace_size", "muon_plan_create", "muon_plan_create_ex", "muon_plan_destroy",
-    "muon_plan_get_info",
-    "muon_step", "muon_stage_momentum", "muon_stage_ns_phase", "muon_stage_apply",
+    "muon_plan_get_info", "muon_plan_table_bytes", "muon_plan_upload",
+    "muon_step", "muon_stage_momentum", "muon_stage_ns_phase",
+    "muon_stage_apply",
     "muon_stage_ns_apply",
     "muon_stage_export_x", "muon_stage_export_norms", "adamw_step", "adamw_step_ex",
     "muon_status_string",
     "muon_last_error", "grad_norm_clip_workspace_size", "grad_norm_clip",
     "state_stats_workspace_size", "state_stats",
-    "muon_clip_plan_create", "muon_clip_plan_destroy", "muon_clip",
+    "muon_clip_plan_create", "muon_clip_plan_destroy", "muon_clip_plan_table_bytes",
+    "muon_clip_plan_upload", "muon_clip",
 ]
 
 MUON_CLIP_FROBENIUS = 0
@@ -126,6 +128,9 @@ def lib() -> ctypes.CDLL:
     L.muon_plan_destroy.argtypes = [P]
     L.muon_plan_destroy.restype = None
     L.muon_plan_get_info.argtypes = [P, ctypes.POINTER(MuonPlanInfo)]
+    L.muon_plan_table_bytes.argtypes = [P]
+    L.muon_plan_table_bytes.restype = SZ
+    L.muon_plan_upload.argtypes = [P, P, SZ, P]
     hp_p = ctypes.POINTER(MuonHParamsC)
     L.muon_step.argtypes = [P, P, P, P, P, SZ, hp_p, P, P]
     L.muon_stage_momentum.argtypes = [P, I32, P, P, P, SZ, hp_p, P]
@@ -148,6 +153,9 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(P), ctypes.POINTER(SZ)]
     L.muon_clip_plan_destroy.argtypes = [P]
     L.muon_clip_plan_destroy.restype = None
+    L.muon_clip_plan_table_bytes.argtypes = [P]
+    L.muon_clip_plan_table_bytes.restype = SZ
+    L.muon_clip_plan_upload.argtypes = [P, P, SZ, P]
     L.muon_clip.argtypes = [P, P, I32, ctypes.c_float, P, P, SZ, P, P, P]
     L.muon_status_string.argtypes = [I32]
     L.muon_status_string.restype = ctypes.c_char_p
@@ -155,7 +163,7 @@ def lib() -> ctypes.CDLL:
     L.muon_last_error.restype = ctypes.c_char_p
     for name in EXPORTED:
         if name not in ("muon_plan_destroy", "muon_clip_plan_destroy", "muon_status_string",
-                        "muon_last_error",
+                        "muon_last_error", "muon_plan_table_bytes", "muon_clip_plan_table_bytes",
                         "grad_norm_clip_workspace_size", "state_stats_workspace_size"):
             getattr(L, name).restype = ctypes.c_int
     _lib_handle = L
@@ -261,7 +269,8 @@ def _ahp(hp, clip=None) -> AdamWHParamsC:
 # ---------------------------------------------------------------- plan
 
 class MuonPlan:
-    """Owns a muon_plan_t (destroyed with the object)."""
+    """Owns a muon_plan_t (destroyed with the object) and, once uploaded, the
+    device tensor holding its tables."""
 
     def __init__(self, handle: int, workspace_bytes: int, n_mats: int, flat_numel: int = 0,
                  param_dtype: int = MUON_DTYPE_BF16, grad_dtype: int = MUON_DTYPE_BF16):
@@ -271,6 +280,21 @@ class MuonPlan:
         self.flat_numel = flat_numel
         self.param_dtype = param_dtype
         self.grad_dtype = grad_dtype
+        self.tables = None
+
+    @property
+    def table_bytes(self) -> int:
+        return muon_plan_table_bytes(self)
+
+    def upload(self, device=None, stream=None) -> None:
+        """Allocate the table buffer on ``device`` (torch's current device if
+        None) and copy the tables into it on ``stream`` (current stream)."""
+        import torch
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        tables = torch.empty(max(1, self.table_bytes), dtype=torch.uint8, device=dev)
+        with torch.cuda.device(tables.device):
+            muon_plan_upload(self, tables, stream)
+        self.tables = tables
 
     def info(self) -> MuonPlanInfo:
         return muon_plan_get_info(self)
@@ -307,11 +331,12 @@ MUON_PLAN_WHOLE_TILES = 2
 
 def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="bf16",
                      workspace_cap: int = 0, tiled_only: bool = False,
-                     whole_tiles: bool = False) -> MuonPlan:
+                     whole_tiles: bool = False, upload: bool = True) -> MuonPlan:
     """tiled_only: every matrix on the tiled NS path (no fused small-matrix
     kernel); whole_tiles: every NS tile computed whole (no split diagonal
-    or edge tiles).
-    Results are bitwise the same either way."""
+    or edge tiles).  Results are bitwise the same either way.
+    upload: copy the tables to a new device tensor on torch's current device
+    and stream (MuonPlan.upload); without it the plan stays host-only."""
     arr = _mats_array(mats)
     h = ctypes.c_void_p(0)
     ws = ctypes.c_size_t(0)
@@ -321,12 +346,28 @@ def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="b
                                      (MUON_PLAN_TILED_ONLY if tiled_only else 0)
                                      | (MUON_PLAN_WHOLE_TILES if whole_tiles else 0),
                                      ctypes.byref(h), ctypes.byref(ws)))
-    return MuonPlan(h.value, ws.value, len(mats), int(flat_numel), dtype_code(param_dtype),
+    plan = MuonPlan(h.value, ws.value, len(mats), int(flat_numel), dtype_code(param_dtype),
                     dtype_code(grad_dtype))
+    if upload:
+        plan.upload()
+    return plan
 
 
 def muon_plan_destroy(plan: MuonPlan) -> None:
     plan.close()
+
+
+def muon_plan_table_bytes(plan: MuonPlan) -> int:
+    return int(lib().muon_plan_table_bytes(ctypes.c_void_p(plan.handle)))
+
+
+def muon_plan_upload(plan: MuonPlan, tables, stream=None) -> None:
+    """tables: a uint8 GPU tensor of at least muon_plan_table_bytes bytes,
+    kept alive by the caller while the plan is used (MuonPlan.upload keeps
+    it on the plan)."""
+    _buf(tables, "tables", muon_plan_table_bytes(plan))
+    _check(lib().muon_plan_upload(ctypes.c_void_p(plan.handle), _ptr(tables), _nbytes(tables),
+                                  _stream(stream)))
 
 
 def muon_plan_get_info(plan: MuonPlan) -> MuonPlanInfo:
@@ -507,7 +548,8 @@ def read_state_stats(out) -> dict:
 # ---------------------------------------------------------------- MuonClip
 
 class MuonClipPlan:
-    """Owns a muon_clip_plan_t (destroyed with the object)."""
+    """Owns a muon_clip_plan_t (destroyed with the object) and, once uploaded,
+    the device tensor holding its tables."""
 
     def __init__(self, handle: int, workspace_bytes: int, n_targets: int, n_groups: int,
                  flat_numel: int, param_dtype: int):
@@ -517,6 +559,17 @@ class MuonClipPlan:
         self.n_groups = n_groups
         self.flat_numel = flat_numel
         self.param_dtype = param_dtype
+        self.tables = None
+
+    def upload(self, device=None, stream=None) -> None:
+        import torch
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        nb = int(lib().muon_clip_plan_table_bytes(ctypes.c_void_p(self.handle)))
+        tables = torch.empty(max(1, nb), dtype=torch.uint8, device=dev)
+        with torch.cuda.device(tables.device):
+            _check(lib().muon_clip_plan_upload(ctypes.c_void_p(self.handle), _ptr(tables),
+                                               _nbytes(tables), _stream(stream)))
+        self.tables = tables
 
     def alloc_workspace(self, device="cuda"):
         import torch
@@ -534,10 +587,11 @@ class MuonClipPlan:
             pass
 
 
-def muon_clip_plan_create(targets, flat_numel: int, param_dtype, n_groups: int = 0
-                          ) -> MuonClipPlan:
+def muon_clip_plan_create(targets, flat_numel: int, param_dtype, n_groups: int = 0,
+                          upload: bool = True) -> MuonClipPlan:
     """targets: (offset, rows, cols[, ld[, group]]) per block (ld defaults
-    to cols, group to 0)."""
+    to cols, group to 0).  upload: copy the tables to a new device tensor on
+    torch's current device and stream."""
     arr = (MuonClipTarget * max(1, len(targets)))()
     for i, t in enumerate(targets):
         off, rows, cols = int(t[0]), int(t[1]), int(t[2])
@@ -549,7 +603,10 @@ def muon_clip_plan_create(targets, flat_numel: int, param_dtype, n_groups: int =
     pd = dtype_code(param_dtype)
     _check(lib().muon_clip_plan_create(arr, len(targets), int(flat_numel), pd, int(n_groups),
                                        ctypes.byref(h), ctypes.byref(ws)))
-    return MuonClipPlan(h.value, ws.value, len(targets), int(n_groups), int(flat_numel), pd)
+    plan = MuonClipPlan(h.value, ws.value, len(targets), int(n_groups), int(flat_numel), pd)
+    if upload:
+        plan.upload()
+    return plan
 
 
 def muon_clip(plan: MuonClipPlan, params, mode, tau: float, max_logits=None, workspace=None,

@@ -183,12 +183,17 @@ using muon::ClipChunk;
 using muon::ClipTarget;
 
 struct muon_clip_plan {
-  int device = 0;
+  int device = -1;       // set by muon_clip_plan_upload
+  bool uploaded = false;
   int32_t n_targets = 0, n_groups = 0, param_dtype = 0;
   int64_t flat_numel = 0;
   int32_t n_chunks = 0;
   size_t ws_bytes = 0;
-  void* d_tables = nullptr;
+  // the block and chunk tables packed as the device sees them, and the
+  // chunk table's byte offset
+  std::vector<char> host_tables;
+  size_t o_chunks = 0;
+  // device copies, inside the caller's table buffer
   ClipTarget* d_targets = nullptr;
   ClipChunk* d_chunks = nullptr;
 };
@@ -283,42 +288,50 @@ int muon_clip_plan_create(const muon_clip_target_t* targets, int32_t n_targets,
   p->flat_numel = flat_numel;
   p->n_chunks = static_cast<int32_t>(dc.size());
   p->ws_bytes = (dc.size() * sizeof(double) + 255) / 256 * 256;
-  hipError_t e = hipGetDevice(&p->device);
-  if (e != hipSuccess) {
-    delete p;
-    return set_hip_error(e, "hipGetDevice");
-  }
   if (n_targets > 0) {
-    const size_t bt = (dt.size() * sizeof(ClipTarget) + 255) / 256 * 256;
-    const size_t total = bt + dc.size() * sizeof(ClipChunk);
-    e = hipMalloc(&p->d_tables, total);
-    if (e != hipSuccess) {
-      delete p;
-      return set_hip_error(e, "hipMalloc(clip tables)");
-    }
-    std::vector<char> host(total, 0);
+    p->o_chunks = (dt.size() * sizeof(ClipTarget) + 255) / 256 * 256;
+    p->host_tables.assign(p->o_chunks + dc.size() * sizeof(ClipChunk), 0);
     std::copy_n(reinterpret_cast<const char*>(dt.data()), dt.size() * sizeof(ClipTarget),
-                host.data());
+                p->host_tables.data());
     std::copy_n(reinterpret_cast<const char*>(dc.data()), dc.size() * sizeof(ClipChunk),
-                host.data() + bt);
-    e = hipMemcpy(p->d_tables, host.data(), total, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      (void)hipFree(p->d_tables);
-      delete p;
-      return set_hip_error(e, "hipMemcpy(clip tables)");
-    }
-    p->d_targets = reinterpret_cast<ClipTarget*>(p->d_tables);
-    p->d_chunks = reinterpret_cast<ClipChunk*>(static_cast<char*>(p->d_tables) + bt);
+                p->host_tables.data() + p->o_chunks);
   }
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
   *out = p;
   return MUON_OK;
 }
 
-void muon_clip_plan_destroy(muon_clip_plan_t* plan) {
-  if (plan == nullptr) return;
-  if (plan->d_tables) (void)hipFree(plan->d_tables);
-  delete plan;
+void muon_clip_plan_destroy(muon_clip_plan_t* plan) { delete plan; }
+
+size_t muon_clip_plan_table_bytes(const muon_clip_plan_t* plan) {
+  return plan == nullptr ? 0 : plan->host_tables.size();
+}
+
+int muon_clip_plan_upload(muon_clip_plan_t* plan, void* tables, size_t table_bytes,
+                          hipStream_t stream) {
+  if (plan == nullptr) return set_error(MUON_ERR_INVALID_ARG, "plan is null");
+  const size_t need = plan->host_tables.size();
+  if (need > 0) {
+    if (tables == nullptr) return set_error(MUON_ERR_INVALID_ARG, "tables is null");
+    if (reinterpret_cast<uintptr_t>(tables) % 256 != 0)
+      return set_error(MUON_ERR_INVALID_ARG, "tables must be 256-byte aligned");
+    if (table_bytes < need)
+      return set_error(MUON_ERR_INVALID_ARG, "tables has " + std::to_string(table_bytes) +
+                                                 " bytes, the plan needs " +
+                                                 std::to_string(need));
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_hip_error(e, "hipGetDevice");
+  if (need > 0) {
+    e = hipMemcpyAsync(tables, plan->host_tables.data(), need, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return set_hip_error(e, "hipMemcpyAsync(clip tables)");
+  }
+  plan->d_targets = reinterpret_cast<ClipTarget*>(tables);
+  plan->d_chunks = reinterpret_cast<ClipChunk*>(static_cast<char*>(tables) + plan->o_chunks);
+  plan->device = dev;
+  plan->uploaded = true;
+  return MUON_OK;
 }
 
 int muon_clip(const muon_clip_plan_t* plan, void* params, int32_t mode, float tau,
@@ -330,6 +343,8 @@ int muon_clip(const muon_clip_plan_t* plan, void* params, int32_t mode, float ta
   if (!std::isfinite(tau) || !(tau > 0.0f))
     return set_error(MUON_ERR_INVALID_ARG, "tau must be finite and > 0");
   if (plan->n_chunks == 0) return MUON_OK;
+  if (!plan->uploaded)
+    return set_error(MUON_ERR_INVALID_ARG, "plan tables are not on a device (muon_clip_plan_upload)");
   if (params == nullptr) return set_error(MUON_ERR_INVALID_ARG, "params is null");
   if (mode == MUON_CLIP_FROBENIUS) {
     if (workspace == nullptr || workspace_bytes < plan->ws_bytes ||

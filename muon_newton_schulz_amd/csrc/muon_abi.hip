@@ -52,8 +52,11 @@ int muon::set_error(int code, const std::string& msg) { return fail(code, msg); 
 int muon::set_hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
 
 struct muon_plan {
-  int device = 0;
-  int n_cu = 256;  // compute units of the plan's device (persistent grid size)
+  // set by muon_plan_upload: the device the tables live on, its compute
+  // units (the persistent grid size)
+  int device = -1;
+  int n_cu = 0;
+  bool uploaded = false;
   int32_t n_mats = 0;
   int64_t flat_numel = 0;
   int32_t param_dtype = 0, grad_dtype = 0, ns_dtype = 0;
@@ -63,8 +66,11 @@ struct muon_plan {
   std::vector<Item> k1_items, syrk_items, bx_items, k7_items;
   std::vector<int32_t> small_list;  // matrices run by the fused small-matrix kernel
   std::vector<Wave> waves;
-  // device copies
-  void* d_tables = nullptr;
+  // the tables packed as the device sees them (built at creation; copied
+  // into the caller's buffer by muon_plan_upload) and their byte offsets
+  std::vector<char> host_tables;
+  size_t o_k1 = 0, o_syrk = 0, o_bx = 0, o_small = 0, o_k7 = 0;
+  // device copies, inside the caller's table buffer
   MatDev* d_mats = nullptr;
   Item* d_k1 = nullptr;
   Item* d_syrk = nullptr;
@@ -324,48 +330,38 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
   return MUON_OK;
 }
 
-int upload_plan(muon_plan& p) {
-  hipError_t e = hipGetDevice(&p.device);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  e = hipDeviceGetAttribute(&p.n_cu, hipDeviceAttributeMultiprocessorCount, p.device);
-  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
-  // the XCD-grouped tile order assumes a grid that is a multiple of the XCD count
-  p.n_cu = p.n_cu >= 8 ? p.n_cu / 8 * 8 : p.n_cu;
+// Pack the tables into one host buffer laid out as the device copy will be
+// (each table 256-byte aligned).  No HIP call.
+void pack_tables(muon_plan& p) {
   const size_t b_mats = align_up(p.mats.size() * sizeof(MatDev), kAlign);
   const size_t b_k1 = align_up(p.k1_items.size() * sizeof(Item), kAlign);
   const size_t b_syrk = align_up(p.syrk_items.size() * sizeof(Item), kAlign);
   const size_t b_bx = align_up(p.bx_items.size() * sizeof(Item), kAlign);
   const size_t b_small = align_up(p.small_list.size() * sizeof(int32_t), kAlign);
   const size_t b_k7 = align_up(p.k7_items.size() * sizeof(Item), kAlign);
-  const size_t total = b_mats + b_k1 + b_syrk + b_bx + b_small + b_k7;
-  if (total == 0) return MUON_OK;
-  e = hipMalloc(&p.d_tables, total);
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc(plan tables)");
-  char* base = static_cast<char*>(p.d_tables);
-  p.d_mats = reinterpret_cast<MatDev*>(base);
-  p.d_k1 = reinterpret_cast<Item*>(base + b_mats);
-  p.d_syrk = reinterpret_cast<Item*>(base + b_mats + b_k1);
-  p.d_bx = reinterpret_cast<Item*>(base + b_mats + b_k1 + b_syrk);
-  p.d_small = reinterpret_cast<int32_t*>(base + b_mats + b_k1 + b_syrk + b_bx);
-  p.d_k7 = reinterpret_cast<Item*>(base + b_mats + b_k1 + b_syrk + b_bx + b_small);
-  std::vector<char> host(total, 0);
-  std::memcpy(host.data(), p.mats.data(), p.mats.size() * sizeof(MatDev));
-  std::memcpy(host.data() + b_mats, p.k1_items.data(), p.k1_items.size() * sizeof(Item));
-  std::memcpy(host.data() + b_mats + b_k1, p.syrk_items.data(), p.syrk_items.size() * sizeof(Item));
-  std::memcpy(host.data() + b_mats + b_k1 + b_syrk, p.bx_items.data(),
-              p.bx_items.size() * sizeof(Item));
-  std::memcpy(host.data() + b_mats + b_k1 + b_syrk + b_bx, p.small_list.data(),
-              p.small_list.size() * sizeof(int32_t));
-  std::memcpy(host.data() + b_mats + b_k1 + b_syrk + b_bx + b_small, p.k7_items.data(),
-              p.k7_items.size() * sizeof(Item));
-  e = hipMemcpy(p.d_tables, host.data(), total, hipMemcpyHostToDevice);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(plan tables)");
-  return MUON_OK;
+  p.o_k1 = b_mats;
+  p.o_syrk = p.o_k1 + b_k1;
+  p.o_bx = p.o_syrk + b_syrk;
+  p.o_small = p.o_bx + b_bx;
+  p.o_k7 = p.o_small + b_small;
+  p.host_tables.assign(p.o_k7 + b_k7, 0);
+  char* h = p.host_tables.data();
+  auto put = [&](size_t off, const void* src, size_t n) {
+    if (n) std::memcpy(h + off, src, n);
+  };
+  put(0, p.mats.data(), p.mats.size() * sizeof(MatDev));
+  put(p.o_k1, p.k1_items.data(), p.k1_items.size() * sizeof(Item));
+  put(p.o_syrk, p.syrk_items.data(), p.syrk_items.size() * sizeof(Item));
+  put(p.o_bx, p.bx_items.data(), p.bx_items.size() * sizeof(Item));
+  put(p.o_small, p.small_list.data(), p.small_list.size() * sizeof(int32_t));
+  put(p.o_k7, p.k7_items.data(), p.k7_items.size() * sizeof(Item));
 }
 
 int check_step_common(const muon_plan_t* plan, int32_t wave, const void* workspace,
                       size_t workspace_bytes) {
   if (plan == nullptr) return fail(MUON_ERR_INVALID_ARG, "plan is null");
+  if (!plan->uploaded)
+    return fail(MUON_ERR_INVALID_ARG, "plan tables are not on a device (muon_plan_upload)");
   if (wave < 0 || wave >= static_cast<int32_t>(plan->waves.size()))
     return fail(MUON_ERR_INVALID_ARG, "wave index out of range");
   if (workspace == nullptr) return fail(MUON_ERR_INVALID_ARG, "workspace is null");
@@ -479,13 +475,13 @@ int muon_plan_create_ex(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_
   *out = nullptr;
   muon_plan* p = new (std::nothrow) muon_plan();
   if (p == nullptr) return fail(MUON_ERR_INVALID_ARG, "out of host memory");
-  int rc = build_plan(mats, n_mats, flat_numel, param_dtype, grad_dtype, ns_dtype,
-                      workspace_cap, flags, *p);
-  if (rc == MUON_OK) rc = upload_plan(*p);
+  const int rc = build_plan(mats, n_mats, flat_numel, param_dtype, grad_dtype, ns_dtype,
+                            workspace_cap, flags, *p);
   if (rc != MUON_OK) {
     muon_plan_destroy(p);
     return rc;
   }
+  pack_tables(*p);
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
   *out = p;
   return MUON_OK;
@@ -498,19 +494,44 @@ int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_num
                              workspace_cap, 0u, out, workspace_bytes);
 }
 
-void muon_plan_destroy(muon_plan_t* plan) {
-  if (plan == nullptr) return;
-  if (plan->d_tables) {
-    int cur = -1;
-    if (hipGetDevice(&cur) == hipSuccess && cur != plan->device) {
-      (void)hipSetDevice(plan->device);
-      (void)hipFree(plan->d_tables);
-      (void)hipSetDevice(cur);
-    } else {
-      (void)hipFree(plan->d_tables);
-    }
+void muon_plan_destroy(muon_plan_t* plan) { delete plan; }
+
+size_t muon_plan_table_bytes(const muon_plan_t* plan) {
+  return plan == nullptr ? 0 : plan->host_tables.size();
+}
+
+int muon_plan_upload(muon_plan_t* plan, void* tables, size_t table_bytes, hipStream_t stream) {
+  if (plan == nullptr) return fail(MUON_ERR_INVALID_ARG, "plan is null");
+  const size_t need = plan->host_tables.size();
+  if (need > 0) {
+    if (tables == nullptr) return fail(MUON_ERR_INVALID_ARG, "tables is null");
+    if (reinterpret_cast<uintptr_t>(tables) % kAlign != 0)
+      return fail(MUON_ERR_INVALID_ARG, "tables must be 256-byte aligned");
+    if (table_bytes < need)
+      return fail(MUON_ERR_INVALID_ARG, "tables has " + std::to_string(table_bytes) +
+                                            " bytes, the plan needs " + std::to_string(need));
   }
-  delete plan;
+  int dev = -1, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+  if (need > 0) {
+    e = hipMemcpyAsync(tables, plan->host_tables.data(), need, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan tables)");
+  }
+  char* base = static_cast<char*>(tables);
+  plan->d_mats = reinterpret_cast<MatDev*>(base);
+  plan->d_k1 = reinterpret_cast<Item*>(base + plan->o_k1);
+  plan->d_syrk = reinterpret_cast<Item*>(base + plan->o_syrk);
+  plan->d_bx = reinterpret_cast<Item*>(base + plan->o_bx);
+  plan->d_small = reinterpret_cast<int32_t*>(base + plan->o_small);
+  plan->d_k7 = reinterpret_cast<Item*>(base + plan->o_k7);
+  plan->device = dev;
+  // the XCD-grouped tile order assumes a grid that is a multiple of the XCD count
+  plan->n_cu = n_cu >= 8 ? n_cu / 8 * 8 : (n_cu > 0 ? n_cu : 1);
+  plan->uploaded = true;
+  return MUON_OK;
 }
 
 int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {

@@ -234,3 +234,70 @@ def test_stage_ns_apply_validates_before_any_hip_call():
     # plan info carries the count of matrices whose update the last NS phase applies
     names = [f[0] for f in M.MuonPlanInfo._fields_]
     assert names[-2:] == ["fused_apply_mats", "reserved"]
+
+
+def test_plans_are_host_only_until_uploaded():
+    # creation makes no HIP call (this container has no GPU) and keeps its
+    # tables in host memory; every step refuses a plan not yet uploaded
+    L = M.lib()
+    mats = (M.MuonMatrix * 2)(M.MuonMatrix(0, 300, 520), M.MuonMatrix(156000, 520, 300))
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+    assert L.muon_plan_create(mats, 2, 312000, 1, 1, 1, 0, ctypes.byref(h),
+                              ctypes.byref(ws)) == M.MUON_OK
+    assert h.value and ws.value > 0
+    nb = L.muon_plan_table_bytes(h)
+    assert nb > 0 and nb % 256 == 0
+    info = M.MuonPlanInfo()
+    assert L.muon_plan_get_info(h, ctypes.byref(info)) == M.MUON_OK and info.n_mats == 2
+    fake = ctypes.c_void_p(1 << 20)
+    hp = M.MuonHParamsC(0.02, 0.1, 0.95, 1, 1.5, -0.5, 0.0, 5, 1e-7, 0, 0.2)
+    assert L.muon_step(h, fake, fake, fake, fake, ws.value, ctypes.byref(hp), None,
+                       None) == M.MUON_ERR_INVALID_ARG
+    assert "muon_plan_upload" in M.muon_last_error()
+    assert L.muon_stage_ns_phase(h, 0, fake, ws.value, ctypes.byref(hp), 0, 1,
+                                 None) == M.MUON_ERR_INVALID_ARG
+    # upload argument checks come before any HIP call
+    assert L.muon_plan_upload(h, None, nb, None) == M.MUON_ERR_INVALID_ARG
+    assert L.muon_plan_upload(h, ctypes.c_void_p((1 << 20) + 8), nb, None) == \
+        M.MUON_ERR_INVALID_ARG                                  # not 256-byte aligned
+    assert L.muon_plan_upload(h, fake, nb - 1, None) == M.MUON_ERR_INVALID_ARG
+    assert L.muon_plan_upload(None, fake, nb, None) == M.MUON_ERR_INVALID_ARG
+    L.muon_plan_destroy(h)
+    assert L.muon_plan_table_bytes(None) == 0
+    # an empty plan has no tables
+    e = ctypes.c_void_p(0)
+    assert L.muon_plan_create(None, 0, 0, 1, 1, 1, 0, ctypes.byref(e), None) == M.MUON_OK
+    assert L.muon_plan_table_bytes(e) == 0
+    L.muon_plan_destroy(e)
+
+
+def test_clip_plans_are_host_only_until_uploaded():
+    L = M.lib()
+    arr = (M.MuonClipTarget * 2)(M.MuonClipTarget(0, 10, 5, 10, 0, 0),
+                                 M.MuonClipTarget(50, 10, 5, 10, 0, 0))
+    h = ctypes.c_void_p(0)
+    ws = ctypes.c_size_t(0)
+    assert L.muon_clip_plan_create(arr, 2, 100, 1, 0, ctypes.byref(h), ctypes.byref(ws)) == \
+        M.MUON_OK
+    nb = L.muon_clip_plan_table_bytes(h)
+    assert nb > 0
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.muon_clip(h, fake, 0, 1.0, None, fake, 1 << 12, None, None, None) == \
+        M.MUON_ERR_INVALID_ARG
+    assert "muon_clip_plan_upload" in M.muon_last_error()
+    assert L.muon_clip_plan_upload(h, None, nb, None) == M.MUON_ERR_INVALID_ARG
+    assert L.muon_clip_plan_upload(h, fake, nb - 1, None) == M.MUON_ERR_INVALID_ARG
+    L.muon_clip_plan_destroy(h)
+
+
+def test_library_allocates_no_device_memory_and_never_synchronises():
+    # the product library's sources (the stand-alone ceiling programs aside)
+    # call no HIP allocator, no blocking copy and no synchronisation
+    csrc = os.path.join(ROOT, "muon_newton_schulz_amd", "csrc")
+    from muon_newton_schulz_amd.build import SOURCES
+    banned = re.compile(r"\bhip(Malloc\w*|Free\w*|HostMalloc|HostAlloc|MallocAsync|Memcpy|"
+                        r"Memset|DeviceSynchronize|StreamSynchronize|EventSynchronize)\s*\(")
+    for f in SOURCES + ["muon_internal.h"]:
+        text = re.sub(r"//[^\n]*", "", open(os.path.join(csrc, f)).read())
+        assert not banned.search(text), (f, banned.search(text).group(0))
