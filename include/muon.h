@@ -244,6 +244,25 @@ int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* m
               void* workspace, size_t workspace_bytes, const muon_hparams_t* hp,
               float* out_update, hipStream_t stream);
 
+/* muon_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is the library's own static device array of
+ * MUON_NOALLOC_WORKSPACE_BYTES (256 MiB), which every GPU the library runs
+ * on holds until the process ends; the call allocates nothing.  The plan's
+ * workspace_bytes must fit in it (create the plan with workspace_cap <=
+ * MUON_NOALLOC_WORKSPACE_BYTES: larger sets of matrices then run in waves),
+ * else MUON_ERR_WORKSPACE_TOO_SMALL and nothing is enqueued.  The plan must
+ * have been uploaded on the current device (which also looks the array's
+ * address up).  Results are bitwise those of muon_step with a workspace of
+ * its own.  Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (as with muon_step, contents on entry are ignored):
+ * calls that overlap on one GPU, on different streams or from different
+ * threads, race and give wrong results; order them on one stream. */
+#define MUON_NOALLOC_WORKSPACE_BYTES ((size_t)256 << 20)
+int muon_step_noalloc(const muon_plan_t* plan, void* params, const void* grads,
+                      float* momentum, const muon_hparams_t* hp, float* out_update,
+                      hipStream_t stream);
+
 /* The stages muon_step enqueues, exposed for stepwise checks and timing.
  * muon_step(...) == for each wave w: muon_stage_momentum(w);
  *   for it in [0, ns_steps): for phase in {1, 2 (only if ns_c != 0), 3}:

@@ -33,7 +33,7 @@ MUON_DTYPE_FP16 = 2
 EXPORTED = [
     "muon_workspace_size", "muon_plan_create", "muon_plan_create_ex", "muon_plan_destroy",
     "muon_plan_get_info", "muon_plan_table_bytes", "muon_plan_upload",
-    "muon_step", "muon_stage_momentum", "muon_stage_ns_phase",
+    "muon_step", "muon_step_noalloc", "muon_stage_momentum", "muon_stage_ns_phase",
     "muon_stage_apply",
     "muon_stage_ns_apply",
     "muon_stage_export_x", "muon_stage_export_norms", "adamw_step", "adamw_step_ex",
@@ -46,6 +46,8 @@ EXPORTED = [
 
 MUON_CLIP_FROBENIUS = 0
 MUON_CLIP_MAX_LOGIT = 1
+# size of the library's static device workspace (muon_step_noalloc)
+MUON_NOALLOC_WORKSPACE_BYTES = 256 << 20
 
 
 class MuonError(RuntimeError):
@@ -133,6 +135,7 @@ def lib() -> ctypes.CDLL:
     L.muon_plan_upload.argtypes = [P, P, SZ, P]
     hp_p = ctypes.POINTER(MuonHParamsC)
     L.muon_step.argtypes = [P, P, P, P, P, SZ, hp_p, P, P]
+    L.muon_step_noalloc.argtypes = [P, P, P, P, hp_p, P, P]
     L.muon_stage_momentum.argtypes = [P, I32, P, P, P, SZ, hp_p, P]
     L.muon_stage_ns_phase.argtypes = [P, I32, P, SZ, hp_p, I32, I32, P]
     L.muon_stage_apply.argtypes = [P, I32, P, P, SZ, hp_p, P, P]
@@ -400,6 +403,19 @@ def muon_step(plan: MuonPlan, params, grads, momentum, workspace, hp, out_update
     _check(lib().muon_step(ctypes.c_void_p(plan.handle), _ptr(params), _ptr(grads),
                            _ptr(momentum), _ptr(workspace), _nbytes(workspace), ctypes.byref(h),
                            _ptr(out_update), _stream(stream)))
+
+
+def muon_step_noalloc(plan: MuonPlan, params, grads, momentum, hp, out_update=None,
+                      stream=None, clip=None) -> None:
+    """muon_step on the library's static device workspace (no workspace
+    argument, nothing allocated); the plan's workspace_bytes must be at most
+    MUON_NOALLOC_WORKSPACE_BYTES (create it with that workspace_cap)."""
+    _flat_args(plan, _buf(params, "params"), _buf(grads, "grads"), _buf(momentum, "momentum"),
+               out_update)
+    h = _hp(hp, clip)
+    _check(lib().muon_step_noalloc(ctypes.c_void_p(plan.handle), _ptr(params), _ptr(grads),
+                                   _ptr(momentum), ctypes.byref(h), _ptr(out_update),
+                                   _stream(stream)))
 
 
 def muon_stage_momentum(plan: MuonPlan, wave: int, grads, momentum, workspace, hp,

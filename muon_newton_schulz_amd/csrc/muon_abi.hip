@@ -6,6 +6,7 @@
 #include <cstddef>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -45,6 +46,39 @@ struct Wave {
   size_t partial_off = 0, norm_off = 0, inv_off = 0;  // byte offsets in the workspace
   size_t bytes = 0;
 };
+
+}  // namespace
+
+// The workspace of muon_step_noalloc: one file-scope device array, which the
+// runtime places on every GPU that loads this library and keeps until the
+// process ends.  In host code its name is a host-side stand-in, not a device
+// address: kernels get the per-device address that hipGetSymbolAddress
+// returns (static_ws_ptr).
+static __device__ __align__(256) unsigned char scratch[MUON_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev` (which must be current),
+// looked up once per device.
+int static_ws_ptr(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MUON_ERR_UNSUPPORTED, "device index beyond the static workspace table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(static workspace)");
+    if (p == nullptr || reinterpret_cast<uintptr_t>(p) % kAlign != 0)
+      return fail(MUON_ERR_HIP, "static workspace address is null or not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MUON_OK;
+}
 
 }  // namespace
 
@@ -531,7 +565,9 @@ int muon_plan_upload(muon_plan_t* plan, void* tables, size_t table_bytes, hipStr
   // the XCD-grouped tile order assumes a grid that is a multiple of the XCD count
   plan->n_cu = n_cu >= 8 ? n_cu / 8 * 8 : (n_cu > 0 ? n_cu : 1);
   plan->uploaded = true;
-  return MUON_OK;
+  // set-up of muon_step_noalloc on this device: its static workspace's address
+  void* ws = nullptr;
+  return static_ws_ptr(dev, &ws);
 }
 
 int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {
@@ -749,6 +785,32 @@ int muon_step(const muon_plan_t* plan, void* params, const void* grads, float* m
     }
   }
   return MUON_OK;
+}
+
+int muon_step_noalloc(const muon_plan_t* plan, void* params, const void* grads,
+                      float* momentum, const muon_hparams_t* hp, float* out_update,
+                      hipStream_t stream) {
+  if (plan == nullptr) return fail(MUON_ERR_INVALID_ARG, "plan is null");
+  if (plan->ws_bytes > MUON_NOALLOC_WORKSPACE_BYTES)
+    return fail(MUON_ERR_WORKSPACE_TOO_SMALL,
+                "plan needs " + std::to_string(plan->ws_bytes) +
+                    " bytes of workspace; the static workspace holds " +
+                    std::to_string(static_cast<size_t>(MUON_NOALLOC_WORKSPACE_BYTES)) +
+                    " (create the plan with workspace_cap <= MUON_NOALLOC_WORKSPACE_BYTES)");
+  if (plan->waves.empty()) return muon_step(plan, params, grads, momentum, nullptr, 0, hp,
+                                            out_update, stream);
+  if (!plan->uploaded)
+    return fail(MUON_ERR_INVALID_ARG, "plan tables are not on a device (muon_plan_upload)");
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(MUON_ERR_INVALID_ARG, "current device differs from the plan's device");
+  void* ws = nullptr;
+  const int rc = static_ws_ptr(dev, &ws);
+  if (rc != MUON_OK) return rc;
+  return muon_step(plan, params, grads, momentum, ws, MUON_NOALLOC_WORKSPACE_BYTES, hp,
+                   out_update, stream);
 }
 
 int adamw_step_ex(void* params, int32_t param_dtype, float* master, const void* grads,
