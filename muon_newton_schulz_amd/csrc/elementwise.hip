@@ -19,6 +19,8 @@
 // All kernels are HBM-bound; accesses are coalesced along the contiguous
 // dimension and reductions use a fixed order, so results are bitwise
 // reproducible run to run.
+#include <type_traits>
+
 #include "muon_internal.h"
 
 namespace muon {
@@ -60,16 +62,15 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Natural padded dims of a matrix: the oriented iterate is [m_pad][n_pad];
-// for a tall matrix that is the transpose of the natural [rows][cols].
-struct NatDims {
-  int rp, cp;  // natural padded rows / cols
-};
-__device__ __forceinline__ NatDims nat_dims(const MatDev& md) {
-  NatDims d;
-  d.rp = md.trans ? md.n_pad : md.m_pad;
-  d.cp = md.trans ? md.m_pad : md.n_pad;
-  return d;
+
+// Index of element (row, col) of a matrix's oriented iterate X in the
+// workspace: the bf16 workspace's 32-column panels (panel_off), or
+// row-major [m_pad][n_pad] for fp32.  Four consecutive columns from a
+// multiple of 4 stay contiguous either way.
+template <typename UT>
+__device__ __forceinline__ int64_t ws_idx(const MatDev& md, int row, int col) {
+  if constexpr (std::is_same<UT, uint16_t>::value) return panel_off(row, col, md.m_pad);
+  else return static_cast<int64_t>(row) * md.n_pad + col;
 }
 
 // 4 consecutive elements (bf16: 8 bytes, fp32: 16 bytes)
@@ -127,7 +128,6 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
   const Item it = items[blockIdx.x];
   const MatDev md = mats[it.mat];
   const int r0 = (it.rc >> 16) * kEwTile, c0 = (it.rc & 0xffff) * kEwTile;
-  const NatDims nd = nat_dims(md);
   UT* X = ws + md.ws_x[0];
   const float omm = 1.0f - mu;
   // the sum of squares in fp64 (fixed order), so the norm keeps full
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
 #pragma unroll
         for (int k = 0; k < 4; ++k) tile[rr][cg + k] = u[k];
       } else {
-        V4<UT>::st(X, static_cast<int64_t>(r) * nd.cp + c, u);
+        V4<UT>::st(X, ws_idx<UT>(md, r, c), u);
       }
     }
     if (md.trans) {
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
       for (int q = 0; q < 4; ++q) {
         const int cc = cc0 + 16 * q;
         const f32x4v v = {tile[rq][cc], tile[rq + 1][cc], tile[rq + 2][cc], tile[rq + 3][cc]};
-        V4<UT>::st(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + rq, v);
+        V4<UT>::st(X, ws_idx<UT>(md, c0 + cc, r0 + rq), v);
       }
     }
   } else {
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
       }
       ss = fma(static_cast<double>(u), static_cast<double>(u), ss);
       if (md.trans) tile[rr][lc] = u;
-      else Elem<UT>::st(X, static_cast<int64_t>(r) * nd.cp + c, u);
+      else Elem<UT>::st(X, ws_idx<UT>(md, r, c), u);
     }
     if (md.trans) {
       // X = U^T: X[c][r], coalesced along r
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
 #pragma unroll 4
       for (int q = 0; q < 16; ++q) {
         const int cc = lr + 4 * q;
-        Elem<UT>::st(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + lc, tile[lc][cc]);
+        Elem<UT>::st(X, ws_idx<UT>(md, c0 + cc, r0 + lc), tile[lc][cc]);
       }
     }
   }
@@ -210,18 +210,17 @@ template <typename UT>
 __device__ __forceinline__ f32x16_t load_nat_tile(const MatDev& md, const UT* X, int r0, int c0,
                                                   float (&tile)[kEwTile][kEwTile + 1]) {
   f32x16_t o;
-  const NatDims nd = nat_dims(md);
   const int lc = threadIdx.x & 63, lr = threadIdx.x >> 6;
   if (!md.trans) {
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-      o[q] = Elem<UT>::ld(X, static_cast<int64_t>(r0 + lr + 4 * q) * nd.cp + c0 + lc);
+      o[q] = Elem<UT>::ld(X, ws_idx<UT>(md, r0 + lr + 4 * q, c0 + lc));
   } else {
     // X[c][r]: read rows c0.. of X along r, transpose in LDS
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int cc = lr + 4 * q;
-      tile[cc][lc] = Elem<UT>::ld(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + lc);
+      tile[cc][lc] = Elem<UT>::ld(X, ws_idx<UT>(md, c0 + cc, r0 + lc));
     }
     __syncthreads();
 #pragma unroll
@@ -322,20 +321,19 @@ __global__ __launch_bounds__(256) void k_apply(const MatDev* __restrict__ mats,
   const ApplyConsts ak = apply_consts(md.rows, md.cols, lr, wd, scale_mode, rms_target);
   if (vec4_ok(md, bufs_aligned)) {
     // thread = 4 consecutive columns x 4 rows (16 elements)
-    const NatDims nd = nat_dims(md);
-    const int cg = (threadIdx.x & 15) * 4, rg = threadIdx.x >> 4;
+      const int cg = (threadIdx.x & 15) * 4, rg = threadIdx.x >> 4;
     f32x4v o[4];
     if (!md.trans) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        o[q] = V4<UT>::ld(X, static_cast<int64_t>(r0 + rg + 16 * q) * nd.cp + c0 + cg);
+        o[q] = V4<UT>::ld(X, ws_idx<UT>(md, r0 + rg + 16 * q, c0 + cg));
     } else {
       // X[c][r]: 4 consecutive r per thread, transposed through LDS
       const int rq = (threadIdx.x & 15) * 4, cc0 = threadIdx.x >> 4;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cc = cc0 + 16 * q;
-        const f32x4v v = V4<UT>::ld(X, static_cast<int64_t>(c0 + cc) * nd.rp + r0 + rq);
+        const f32x4v v = V4<UT>::ld(X, ws_idx<UT>(md, c0 + cc, r0 + rq));
 #pragma unroll
         for (int k = 0; k < 4; ++k) tile[rq + k][cc] = v[k];
       }

@@ -25,6 +25,18 @@ constexpr int kSmallElems = 32768;
 // to the tiles that share their operand panels.
 constexpr int kDiagInPlaceMaxTiles = 8;
 
+// Layout of the bf16 NS workspace.  Every matrix there (the iterates X,
+// A and B; all have m_pad rows) is stored as panels of 32 columns: panel q
+// holds columns 32q..32q+31 of every row, row-major, so element (r, c) is at
+// ((c / 32) * m_pad + r) * 32 + c % 32.  A pipeline stage of the NS GEMMs
+// (256 rows x 32 k of an operand read along its rows) is then 16 KiB of
+// contiguous memory and its loads read whole 128-byte lines.  The fp32
+// workspace stays row-major ([m_pad][ld]).
+constexpr int kPanelCols = 32;
+__host__ __device__ __forceinline__ int64_t panel_off(int64_t r, int64_t c, int64_t rows) {
+  return ((c >> 5) * rows + r) * kPanelCols + (c & 31);
+}
+
 // One matrix of a plan, as the device sees it.  "Oriented" dims put the
 // short side first (m = min(rows, cols), n = max(rows, cols)); tall
 // matrices (rows > cols) are iterated transposed.  The NS iterate X is

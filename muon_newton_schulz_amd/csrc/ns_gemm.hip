@@ -11,8 +11,12 @@
 //   phase 3  X' = xs * (B X)         the a X term is folded into B's diagonal
 // On the first iteration s2 = inv^2 and xs = inv, which folds the
 // Frobenius normalisation X0 = U/(||U||_F + eps) into the epilogues.
-// X lives in two ping-pong buffers (m x n, row-major, padded; the padding
-// inside the contraction extents m_k, n_k is zero).
+// X lives in two ping-pong buffers (m x n, padded; the padding inside the
+// contraction extents m_k, n_k is zero).  X, A and B are stored as panels
+// of 32 columns (panel_off in muon_internal.h): one stage of 256 rows x 32
+// k of an operand read along its rows is 16 KiB of contiguous memory, so
+// the operand loads read whole 128-byte lines (row-major storage gave each
+// load instruction 16 half lines).
 // The last phase 3 of a step can instead apply the update to the
 // parameters, W <- (1 - lr wd) W - lr s O with O the bf16 value X' would
 // hold (k_ns_bf16_apply; optimizer tutorial 3.1, decoupled decay).
@@ -239,27 +243,29 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     if (md.fuse && g.clip != nullptr && g.clip->skip) return;
   uint16_t* ws = static_cast<uint16_t*>(g.ws);
 
-  // operands
+  // operands, in the panel layout of the workspace (panel_off): P and, in
+  // phases 1 and 2, Q are read along their rows, one 32-column panel per
+  // stage, so P (Q) points at row ti*256 (tj*256) of panel 0 and a stage
+  // advances by one panel, PS elements.  Phase 3's Q = X is read as [k][j]:
+  // Q points at panel 8*tj (column tj*256), row 0, and a stage advances by
+  // 32 rows.
   const uint16_t *P, *Q;
-  int ldp, ldq, K;
+  int K;
+  const int64_t PS = static_cast<int64_t>(md.m_pad) * kPanelCols;  // elements per panel
   // K runs over the true extent rounded to the K step only: the rest of
   // the padded operands is zero
   if (PHASE == 1) {
-    ldp = ldq = md.n_pad;
     K = md.n_k;
-    P = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(ti) * BT * ldp;
-    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * BT * ldq;
+    P = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(ti) * BT * kPanelCols;
+    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * BT * kPanelCols;
   } else if (PHASE == 2) {
-    ldp = ldq = md.m_pad;
     K = md.m_k;
-    P = ws + md.ws_a + static_cast<int64_t>(ti) * BT * ldp;
-    Q = ws + md.ws_a + static_cast<int64_t>(tj) * BT * ldq;
+    P = ws + md.ws_a + static_cast<int64_t>(ti) * BT * kPanelCols;
+    Q = ws + md.ws_a + static_cast<int64_t>(tj) * BT * kPanelCols;
   } else {
-    ldp = md.m_pad;
     K = md.m_k;
-    ldq = md.n_pad;
-    P = ws + md.ws_b + static_cast<int64_t>(ti) * BT * ldp;
-    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * BT;  // column block of [k][j]
+    P = ws + md.ws_b + static_cast<int64_t>(ti) * BT * kPanelCols;
+    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * (BT / kPanelCols) * PS;
   }
 
   const int t = threadIdx.x, lane = t & 63;
@@ -358,19 +364,22 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
   // DMA of one stage, one instruction at a time: instruction D (0..7) of
-  // this wave; D < 4: 16 P rows of 64 bytes (16-byte chunk c of row r at
-  // position c ^ ((r >> 2) & 3)), D >= 4: the same for Q (phases 1, 2) or
-  // 2 k-rows of 512 bytes of Q (phase 3, 32-column block q of k-row r at
-  // q ^ (r & 3)).  The per-lane source offsets are fixed for the tile.
+  // this wave; D < 4: 16 P rows of 64 bytes, 1 KiB contiguous in the
+  // panel (16-byte chunk c of row r at LDS position c ^ ((r >> 2) & 3)),
+  // D >= 4: the same for Q (phases 1, 2) or 2 k-rows of 512 bytes of Q
+  // (phase 3: 32-column block q of k-row r, the 64-byte row r of panel q,
+  // at LDS position q ^ (r & 3); rows r and r + 1 of a panel make one
+  // 128-byte line).  The per-lane source offsets are fixed for the tile.
   const char* Pc = reinterpret_cast<const char*>(P);
   const char* Qc = reinterpret_cast<const char*>(Q);
   const int pc = (lane & 3) ^ ((lane >> 4) & 3);
-  const uint32_t dP = ((lane >> 2) * ldp + 8 * pc) * 2;
-  const uint32_t dQ = ((lane >> 2) * ldq + 8 * pc) * 2;
+  const uint32_t dPQ = ((lane >> 2) * kPanelCols + 8 * pc) * 2;
   uint32_t dQ3[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-    dQ3[par] = ((lane >> 5) * ldq + 8 * ((lane & 31) ^ (((2 * par + (lane >> 5)) & 3) << 2))) * 2;
+  for (int par = 0; par < 2; ++par) {
+    const int jl = 8 * ((lane & 31) ^ (((2 * par + (lane >> 5)) & 3) << 2));  // column in the tile
+    dQ3[par] = static_cast<uint32_t>(((jl >> 5) * PS + (lane >> 5) * kPanelCols + (jl & 31)) * 2);
+  }
   auto issue_dma = [&](int kt, int slot, auto d_c) {
     constexpr int D = decltype(d_c)::value, U = D & 3;
     if constexpr (D >= DPS) return;  // shared P and Q: no Q copy
@@ -378,16 +387,16 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
       if (dma_half) return;  // padding rows of P (ROLE 3) or Q (ROLE 4)
     uint16_t* sp = smem + slot * 2 * BT * BK;
     uint16_t* sq = sp + BT * BK;
-    const int64_t k0 = static_cast<int64_t>(kt) * BK;
     if constexpr (D < 4) {
       const int R0 = (wave * 4 + U) * 16;
-      dma16(Pc + (static_cast<int64_t>(R0) * ldp + k0) * 2, dP, sp + R0 * BK);
+      dma16(Pc + (kt * PS + R0 * kPanelCols) * 2, dPQ, sp + R0 * BK);
     } else if constexpr (PHASE != 3) {
       const int R0 = (wave * 4 + U) * 16;
-      dma16(Qc + (static_cast<int64_t>(R0) * ldq + k0) * 2, dQ, sq + R0 * BK);
+      dma16(Qc + (kt * PS + R0 * kPanelCols) * 2, dPQ, sq + R0 * BK);
     } else {
       const int R0 = (wave * 4 + U) * 2;
-      dma16(Qc + (k0 + R0) * static_cast<int64_t>(ldq) * 2, dQ3[U & 1], sq + R0 * BT);
+      dma16(Qc + (static_cast<int64_t>(kt) * BK + R0) * kPanelCols * 2, dQ3[U & 1],
+            sq + R0 * BT);
     }
   };
 
@@ -483,11 +492,10 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   u32x4_t apre[32];
   if constexpr (aterm) {
     const int pl = opaque_lane(lane);
-    const uint16_t* Ao =
-        ws + md.ws_a + static_cast<int64_t>(i0w + (pl >> 4)) * md.m_pad + j0w + 8 * (pl & 15);
+    const uint16_t* Ao = ws + md.ws_a + panel_off(i0w + (pl >> 4), j0w + 8 * (pl & 15), md.m_pad);
 #pragma unroll
     for (int u = 0; u < 32; ++u)
-      apre[u] = *reinterpret_cast<const u32x4_t*>(Ao + static_cast<int64_t>(4 * u) * md.m_pad);
+      apre[u] = *reinterpret_cast<const u32x4_t*>(Ao + 4 * u * kPanelCols);
   }
   if constexpr (APPLY) {
     if (w_rows) {
@@ -518,16 +526,13 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // (and spill).
   const int elane = opaque_lane(lane);
   uint16_t* S = smem + wave * (128 * 128);
-  uint16_t* C;
-  int ldc;
+  uint16_t* C;  // result, panel layout with m_pad rows
   bool mirror;
   if (PHASE == 3) {
     C = ws + (g.x_cur ? md.ws_x[0] : md.ws_x[1]);
-    ldc = md.n_pad;
     mirror = false;
   } else {
     C = ws + ((PHASE == 1 && g.c != 0.0f) ? md.ws_a : md.ws_b);
-    ldc = md.m_pad;
     mirror = true;  // off-diagonal tiles whole, diagonal tiles block by block
   }
 
@@ -688,7 +693,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     if (ROLE >= 2 && rc >= 8) continue;
     u32x4_t v = *reinterpret_cast<const u32x4_t*>(S + row_slot16(u));
     if (u & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
-    *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(i0w + r) * ldc + j0w + 8 * rc) = v;
+    *reinterpret_cast<u32x4_t*>(C + panel_off(i0w + r, j0w + 8 * rc, md.m_pad)) = v;
   }
 
   // mirror piece u (rows 16*(u/4).., columns 32*(u%4).. of the staged
@@ -724,7 +729,7 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
         const int jb = (u & 3) * 32, ib = (u >> 2) * 16;
         const int jo = jb + 16 * (G & 1) + s;
         const int io = ib + 8 * (G >> 1);
-        *reinterpret_cast<s16x8_t*>(C + static_cast<int64_t>(j0w + jo) * ldc + i0w + io) =
+        *reinterpret_cast<s16x8_t*>(C + panel_off(j0w + jo, i0w + io, md.m_pad)) =
             __builtin_shufflevector(tr[2 * v], tr[2 * v + 1], 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }

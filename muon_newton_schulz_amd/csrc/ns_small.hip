@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void k_ns_small(GemmArgs g, const int32_t* __r
       const int v = threadIdx.x + 256 * u;
       if (v < mk * c8) {
         const int r = v / c8, c = (v - r * c8) * 8;
-        buf[u] = *reinterpret_cast<const u32x4_t*>(Xin + static_cast<int64_t>(r) * md.n_pad + c);
+        buf[u] = *reinterpret_cast<const u32x4_t*>(Xin + panel_off(r, c, md.m_pad));
       }
     }
 #pragma unroll
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void k_ns_small(GemmArgs g, const int32_t* __r
   __syncthreads();
   for (int v = threadIdx.x; v < mk * c8; v += 256) {
     const int r = v / c8, c = (v - r * c8) * 8;
-    *reinterpret_cast<u32x4_t*>(Xout + static_cast<int64_t>(r) * md.n_pad + c) =
+    *reinterpret_cast<u32x4_t*>(Xout + panel_off(r, c, md.m_pad)) =
         *reinterpret_cast<const u32x4_t*>(sx + r * ldx + c);
   }
 }
