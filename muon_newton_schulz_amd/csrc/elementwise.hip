@@ -106,6 +106,27 @@ __device__ __forceinline__ bool vec4_ok(const MatDev& md, int bufs_aligned) {
   return bufs_aligned && (md.off & 3) == 0 && (md.cols & 3) == 0;
 }
 
+// Span path of the apply kernel for a matrix whose rows are off that grid
+// (an odd offset or width in the flat concatenation): row rr of a 64x64
+// tile is the flat span [a, b) of the parameter-side buffers.  Its whole aligned 4-element groups,
+// [fs, fe), at most 16, are read and written 4-wide, 16 threads per row;
+// the head [a, min(fs, b)) and the tail [max(fs, fe), b), at most 3
+// elements each, one at a time, 4 threads per row, so that neither pass
+// branches on the data.  The iterate side goes through the LDS tile.
+struct Span {
+  int64_t a, b;    // flat elements of the row in the tile: [a, b), empty past the matrix
+  int64_t fs, fe;  // whole 4-element groups: [fs, fe) (empty if fe <= fs)
+};
+__device__ __forceinline__ Span tile_row_span(const MatDev& md, int r, int c0) {
+  Span sp;
+  const int w = (r < md.rows && c0 < md.cols) ? min(kEwTile, md.cols - c0) : 0;
+  sp.a = md.off + static_cast<int64_t>(r) * md.cols + c0;
+  sp.b = sp.a + w;
+  sp.fs = (sp.a + 3) & ~int64_t{3};
+  sp.fe = sp.b & ~int64_t{3};
+  return sp;
+}
+
 // One 64x64 tile (natural coordinates) of one matrix per block, covering
 // the padded extent so the zero padding of the NS operand is (re)written
 // every step.  4-wide path: thread = 4 consecutive columns x 4 rows.
@@ -199,7 +220,13 @@ __global__ __launch_bounds__(256) void k_momentum(const MatDev* __restrict__ mat
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
   __syncthreads();
-  if (threadIdx.x == 0) partials[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  // the partial's slot is the tile's place in its matrix's row-major tile
+  // order (the launch order of the tiles is permuted over the XCDs)
+  if (threadIdx.x == 0) {
+    const int ctiles = (md.trans ? md.m_pad : md.n_pad) / kEwTile;
+    partials[md.k1_begin + static_cast<int64_t>(it.rc >> 16) * ctiles + (it.rc & 0xffff)] =
+        (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  }
 }
 
 // Reads the 64x64 natural-coordinate tile (r0, c0) of the oriented iterate
@@ -356,6 +383,63 @@ __global__ __launch_bounds__(256) void k_apply(const MatDev* __restrict__ mats,
         for (int k = 0; k < 4; ++k) wn[k] = apply_one(ak, w[k], oo[k]);
         V4<PT>::st(params, e, wn);
         if (out_update) V4<float>::st(out_update, e, oo);
+      }
+    }
+    return;
+  }
+  if (bufs_aligned) {
+    // span path: O of the tile into LDS in natural coordinates, then the
+    // parameter-side buffers in aligned groups
+    {
+      const int q4 = (threadIdx.x & 15) * 4, q16 = threadIdx.x >> 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (!md.trans) {
+          const int rr = q16 + 16 * q;
+          const f32x4v v = V4<UT>::ld(X, ws_idx<UT>(md, r0 + rr, c0 + q4));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) tile[rr][q4 + k] = v[k] * osc;
+        } else {
+          const int cc = q16 + 16 * q;
+          const f32x4v v = V4<UT>::ld(X, ws_idx<UT>(md, c0 + cc, r0 + q4));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) tile[q4 + k][cc] = v[k] * osc;
+        }
+      }
+    }
+    __syncthreads();
+    {
+      const int gi = threadIdx.x & 15, q16 = threadIdx.x >> 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = q16 + 16 * q;
+        const Span sp = tile_row_span(md, r0 + rr, c0);
+        const int64_t gs = sp.fs + 4 * gi;
+        if (gs + 4 > sp.fe) continue;
+        const int cc = static_cast<int>(gs - sp.a);
+        f32x4v oo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) oo[k] = tile[rr][cc + k];
+        const f32x4v w = V4<PT>::ld(params, gs);
+        f32x4v wn;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wn[k] = apply_one(ak, w[k], oo[k]);
+        V4<PT>::st(params, gs, wn);
+        if (out_update) V4<float>::st(out_update, gs, oo);
+      }
+    }
+    {
+      const int rr = threadIdx.x >> 2, j = threadIdx.x & 3;
+      const Span sp = tile_row_span(md, r0 + rr, c0);
+      const int64_t eh = sp.a + j, et = (sp.fe > sp.fs ? sp.fe : sp.fs) + j;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t e = h == 0 ? eh : et;
+        const bool mine = h == 0 ? (e < sp.fs && e < sp.b) : (e < sp.b);
+        if (!mine) continue;
+        const float oo = tile[rr][static_cast<int>(e - sp.a)];
+        Elem<PT>::st(params, e, apply_one(ak, Elem<PT>::ld(params, e), oo));
+        if (out_update) out_update[e] = oo;
       }
     }
     return;

@@ -152,6 +152,24 @@ std::vector<Item> xcd_dispatch_order(const std::vector<Item>& logical) {
   return out;
 }
 
+// Launch order of an elementwise tile list: workgroup b runs on XCD b % 8,
+// and XCD x receives a contiguous run of the list, in order.  Neighbouring
+// tiles of a row band share the cache lines at their boundary when a
+// matrix's rows are off the line grid (ragged offsets and widths); in this
+// order both tiles go through the same L2, close in time, instead of two.
+std::vector<Item> xcd_contiguous_order(const std::vector<Item>& logical) {
+  const int64_t n = static_cast<int64_t>(logical.size());
+  std::vector<Item> out(logical.size());
+  const int64_t q = n / kXcds, rem = n % kXcds;
+  int64_t start[kXcds];
+  for (int64_t x = 0, s = 0; x < kXcds; ++x) {
+    start[x] = s;
+    s += q + (x < rem ? 1 : 0);
+  }
+  for (int64_t b = 0; b < n; ++b) out[static_cast<size_t>(b)] = logical[static_cast<size_t>(start[b % kXcds] + b / kXcds)];
+  return out;
+}
+
 // Tiles of one matrix (rows x cols tiles; upper triangle only if tri) in
 // super-tile order: kSuperRows x kSuperCols blocks, row-major, so that
 // consecutive tiles share their row and column operand panels.
@@ -318,9 +336,17 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     }
     w.k1_count = static_cast<int64_t>(p.k1_items.size()) - w.k1_begin;
     w.k7_begin = static_cast<int64_t>(p.k7_items.size());
+    std::vector<Item> k7_l;
     for (int64_t k = w.k1_begin; k < w.k1_begin + w.k1_count; ++k)
-      if (!p.mats[p.k1_items[k].mat].fuse) p.k7_items.push_back(p.k1_items[k]);
+      if (!p.mats[p.k1_items[k].mat].fuse) k7_l.push_back(p.k1_items[k]);
+    const std::vector<Item> k7 = xcd_contiguous_order(k7_l);
+    p.k7_items.insert(p.k7_items.end(), k7.begin(), k7.end());
     w.k7_count = static_cast<int64_t>(p.k7_items.size()) - w.k7_begin;
+    {
+      const std::vector<Item> k1_l(p.k1_items.begin() + w.k1_begin, p.k1_items.end());
+      const std::vector<Item> k1 = xcd_contiguous_order(k1_l);
+      std::copy(k1.begin(), k1.end(), p.k1_items.begin() + w.k1_begin);
+    }
     w.bytes = off;
     ws_max = std::max(ws_max, off);
 

@@ -559,3 +559,41 @@ def test_extreme_gradient_scales_normalise_like_the_oracle(gpu, g_std, eps):
         M.muon_stage_export_norms(s.plan, 0, s.ws, norms)
         torch.cuda.synchronize()
         assert np.isfinite(np64(norms)).all() and (np64(norms) > 0).all()
+
+
+def test_span_path_matches_the_scalar_path(gpu):
+    # Matrices at odd offsets or widths in an aligned buffer take the apply
+    # kernel's span path (aligned 4-element groups of each tile row of W);
+    # the same matrices in buffers shifted by one element (no 4-element
+    # alignment anywhere) take its one-element path.  Both compute the same
+    # expression per element, and the momentum and NS kernels take the same
+    # paths in both layouts, so W, M and O agree bitwise.
+    shapes = [(37, 129), (129, 37), (300, 517), (517, 300), (64, 65), (1000, 7)]
+    mats, n = _flat(shapes, gap=5)
+    hp = mhp(QUINTIC)
+    res = []
+    for shift in (0, 1):
+        g = torch.Generator(device=gpu)
+        g.manual_seed(41)
+        P = torch.zeros(n + 8, dtype=torch.bfloat16, device=gpu)
+        G = torch.zeros(n + 8, dtype=torch.bfloat16, device=gpu)
+        Mo = torch.zeros(n + 8, device=gpu)
+        out = torch.zeros(n + 8, device=gpu)
+        vals = [(torch.randn(r * c, generator=g, device=gpu) * 0.02,
+                 torch.randn(r * c, generator=g, device=gpu) * 0.02,
+                 torch.randn(r * c, generator=g, device=gpu) * 1e-3) for (o, r, c) in mats]
+        for (o, r, c), (w, gr, m) in zip(mats, vals):
+            P[shift + o:shift + o + r * c] = w.to(torch.bfloat16)
+            G[shift + o:shift + o + r * c] = gr.to(torch.bfloat16)
+            Mo[shift + o:shift + o + r * c] = m
+        plan = M.muon_plan_create(mats, n, "bf16", "bf16", "bf16")
+        ws = plan.alloc_workspace(gpu)
+        for with_out in (True, False):
+            M.muon_step(plan, P[shift:shift + n], G[shift:shift + n], Mo[shift:shift + n], ws, hp,
+                        out[shift:shift + n] if with_out else None)
+        torch.cuda.synchronize()
+        res.append((P[shift:shift + n].clone(), Mo[shift:shift + n].clone(),
+                    out[shift:shift + n].clone()))
+    (P0, M0, O0), (P1, M1, O1) = res
+    assert torch.equal(M0, M1) and torch.equal(O0, O1)
+    assert torch.equal(P0.view(torch.int16), P1.view(torch.int16))
