@@ -239,9 +239,9 @@ def cpu_baseline(wl, hp, flop_budget, adam_n):
 
 def parity_matrices(wl):
     """Matrices the oracle checks at the first and last step: the smallest
-    whose offset and cols are multiples of 8 (the update fused into the last
-    NS phase, with bf16 parameters) and the smallest of the others (the
-    separate apply kernel)."""
+    whose offset and cols are multiples of 8 and the smallest of the others
+    (with bf16 parameters both take the update fused into the last NS phase,
+    the second with its rows realigned onto the 8-element grid)."""
     mats = wl.mats()
     size = lambda i: mats[i][1] * mats[i][2]  # noqa: E731
     on8 = [i for i, (o, r, c) in enumerate(mats) if o % 8 == 0 and c % 8 == 0]

@@ -285,13 +285,14 @@ int muon_stage_apply(const muon_plan_t* plan, int32_t wave, void* params, void* 
                      hipStream_t stream);
 /* muon_stage_ns_phase(w, ns_steps - 1, 3) followed by muon_stage_apply(w)
  * with out_update NULL, bitwise, in fewer HBM passes: with bf16 NS and
- * bf16 params in a 16-byte aligned buffer, every matrix whose offset and
- * cols are multiples of 8 (muon_plan_info_t.fused_apply_mats) has its
- * update applied by the phase-3 epilogue, which reads and writes W instead
- * of writing X (X of the last iteration is then not in the workspace;
- * muon_stage_export_x must not be asked for it); the others run the apply
- * kernel.  ns_steps must be >= 1.  With hp->clip->skip set, params are
- * left unchanged. */
+ * bf16 params in a 16-byte aligned buffer, every tiled matrix
+ * (muon_plan_info_t.fused_apply_mats; any offset and cols) has its update
+ * applied by the phase-3 epilogue, which reads and writes W instead of
+ * writing X (X of the last iteration is then not in the workspace;
+ * muon_stage_export_x must not be asked for it); the small matrices run
+ * the apply kernel, and so does every matrix when the buffer is not
+ * 16-byte aligned.  ns_steps must be >= 1.  With hp->clip->skip set,
+ * params are left unchanged. */
 int muon_stage_ns_apply(const muon_plan_t* plan, int32_t wave, void* params, void* workspace,
                         size_t workspace_bytes, const muon_hparams_t* hp, hipStream_t stream);
 

@@ -252,11 +252,11 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                   : 0;
     d.split = (ns_dtype == MUON_DTYPE_BF16 && !d.small && !(flags & MUON_PLAN_WHOLE_TILES)) ? 1 : 0;
     // the fused update writes 16-byte pieces of 8 parameters along a
-    // natural row
-    d.fuse = (ns_dtype == MUON_DTYPE_BF16 && param_dtype == MUON_DTYPE_BF16 && !d.small &&
-              d.off % 8 == 0 && d.cols % 8 == 0)
-                 ? 1
-                 : 0;
+    // natural row: from the staged tile when the rows are on the flat
+    // buffer's 8-element grid (1), realigned per row otherwise (2)
+    const bool fusable =
+        ns_dtype == MUON_DTYPE_BF16 && param_dtype == MUON_DTYPE_BF16 && !d.small;
+    d.fuse = !fusable ? 0 : (d.off % 8 == 0 && d.cols % 8 == 0) ? 1 : 2;
     const double m = std::min(d.rows, d.cols), n = std::max(d.rows, d.cols);
     p.flops_per_iter += m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n;
   }
@@ -612,7 +612,7 @@ int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {
   info->fused_apply_mats = 0;
   for (const muon::MatDev& d : plan->mats) {
     info->split_tile_mats += d.split;
-    info->fused_apply_mats += d.fuse;
+    info->fused_apply_mats += d.fuse != 0;
   }
   info->reserved = 0;
   return MUON_OK;

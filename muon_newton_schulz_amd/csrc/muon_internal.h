@@ -56,9 +56,10 @@ struct MatDev {
   int32_t split;         // 1: split tiles (diagonal tiles of the symmetric
                          // products, half-empty edge tiles) share their
                          // work out over the waves
-  int32_t fuse;          // 1: the last phase 3 can apply the update to W in
-                         // its epilogue (tiled bf16 NS, bf16 params, offset
-                         // and cols multiples of 8)
+  int32_t fuse;          // the last phase 3 can apply the update to W in
+                         // its epilogue (tiled bf16 NS, bf16 params): 1 when
+                         // offset and cols are multiples of 8, 2 otherwise
+                         // (W rows realigned onto the 8-element grid)
   int32_t reserved;
   // element offsets (in NS elements) into the workspace
   int64_t ws_x[2];       // X : m_pad x n_pad, ping-pong

@@ -202,6 +202,23 @@ __device__ __forceinline__ int stg(int i, int j) {
   return i * 128 + ((((j >> 2) ^ g) & 31) << 2);
 }
 
+// Eight consecutive staged values of row i from any column c (c <= 120):
+// the three 4-element slots from c/4 on, shifted by c%4 elements.
+__device__ __forceinline__ u32x4_t stg_read8(const uint16_t* S, int i, int c) {
+  const int a = c & ~3, b = c & 3;
+  const u32x2_t s0 = *reinterpret_cast<const u32x2_t*>(S + stg(i, a));
+  const u32x2_t s1 = *reinterpret_cast<const u32x2_t*>(S + stg(i, a + 4));
+  const u32x2_t s2 = *reinterpret_cast<const u32x2_t*>(S + stg(i, a + 8 < 128 ? a + 8 : 124));
+  const uint32_t w[6] = {s0[0], s0[1], s1[0], s1[1], s2[0], s2[1]};
+  const uint32_t sh = (b & 1) * 16;  // element b starts in word b/2 at bit 16 (b%2)
+  u32x4_t o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    o[k] = (b >> 1) ? __builtin_amdgcn_alignbit(w[k + 2], w[k + 1], sh)
+                    : __builtin_amdgcn_alignbit(w[k + 1], w[k], sh);
+  return o;
+}
+
 // Split tiles.  Diagonal tiles of the symmetric products (phases 1, 2) need
 // only the 36 upper 32x32 blocks of their 8x8.  ROLE 1, waves (0,0) and
 // (1,1): the upper blocks of their quadrant (bi <= bj, 10 of 16).  ROLE 2:
@@ -225,6 +242,138 @@ __device__ __forceinline__ int tile_role(int phase, const MatDev& md, int ti, in
   if (phase == 3 && m - ti * BT <= BT / 2) return 3;
   if ((phase == 3 ? n : m) - tj * BT <= BT / 2) return 4;
   return 0;
+}
+
+// The fused update of a matrix whose W rows are off the flat buffer's
+// 8-element grid (offset or cols not a multiple of 8).  A W row of the
+// wave's sub-tile is a tile row (wide matrix) or a tile column (tall
+// matrix): W row RB + r, r < 128 (64 rows of a tall matrix's split-role
+// wave), columns CB .. CB + len - 1.  Its flat range splits into 16-byte
+// pieces on the grid (piece t at column c0 + 8t) and at most 7 + 7
+// parameters before and after them, written one by one (2-byte stores
+// touch no parameter of a neighbouring tile).  Lane slot u takes row
+// r = lane/16 + 4u: piece t = lane % 16, and the parameter t before the
+// pieces (t < 8) or t - 8 after them.  After the staging, every W load
+// goes out first (offgrid_load, then the single parameters'), and O is
+// read at the same positions (offgrid_update); holding W in registers
+// across the last K stage or the staging loop spilled.  A tall matrix's W
+// row is a staged column, read one value per row.  Same arithmetic as the
+// apply kernel:
+// W' = fma(-step, O, decay W) rounded to bf16.  The 16-byte alignment of
+// the parameter buffer is the caller's (the host checks it).
+struct OffgridRow {
+  const uint16_t* base;  // params + row0(u), wave-uniform
+  int r, lo, c0, np, hn, ts, tn;
+};
+struct OffgridTile {
+  int RB, CB, nrows, len;
+};
+template <int ROLE>
+__device__ __forceinline__ OffgridTile offgrid_tile(const MatDev& md, int i0w, int j0w) {
+  constexpr int WC = ROLE >= 2 ? 64 : 128;  // a split-role wave's tile columns
+  OffgridTile tl;
+  tl.RB = md.trans ? j0w : i0w;
+  tl.CB = md.trans ? i0w : j0w;
+  tl.nrows = md.trans ? WC : 128;
+  tl.len = min(tl.CB + (md.trans ? 128 : WC), md.cols) - tl.CB;
+  return tl;
+}
+// Row r = ln/16 + 4u starts at flat element row0(u) + lo, with the
+// wave-uniform row0(u) = off + (RB + 4u) cols + CB and the lane part
+// lo = (ln/16) cols; everything per lane is 32-bit.  s: the row's shift off
+// the grid, c0 = (8 - s) % 8 its first piece, np pieces, hn parameters
+// before them and tn after them from column ts.  Each pass derives ln from
+// its own opaque copy of the lane id, so that these values are recomputed
+// rather than kept live from one pass to the next.
+__device__ __forceinline__ bool offgrid_row(const MatDev& md, const OffgridTile& tl,
+                                            const uint16_t* params, int ln, int u,
+                                            OffgridRow& q) {
+  q.r = (ln >> 4) + 4 * u;
+  if (tl.len <= 0 || q.r >= tl.nrows || tl.RB + q.r >= md.rows) return false;
+  const int64_t row0 = md.off + static_cast<int64_t>(tl.RB + 4 * u) * md.cols + tl.CB;
+  q.base = params + row0;
+  q.lo = (ln >> 4) * md.cols;
+  const int sft = (static_cast<int>(row0 & 7) + (q.lo & 7)) & 7;
+  q.c0 = (8 - sft) & 7;
+  q.hn = min(q.c0, tl.len);
+  q.np = tl.len > q.c0 ? (tl.len - q.c0) >> 3 : 0;
+  q.ts = q.c0 + 8 * q.np;
+  q.tn = tl.len - q.ts;
+  return true;
+}
+__device__ __forceinline__ bool offgrid_single(const OffgridRow& q, int t, int& c) {
+  c = t < 8 ? t : q.ts + t - 8;
+  return t < 8 ? t < q.hn : t - 8 < q.tn;
+}
+template <int ROLE>
+__device__ __forceinline__ void offgrid_load(const MatDev& md, const uint16_t* params, int i0w,
+                                             int j0w, int lane, u32x4_t* wv) {
+  const OffgridTile tl = offgrid_tile<ROLE>(md, i0w, j0w);
+  const int ln = opaque_lane(lane), t = ln & 15;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    OffgridRow q;
+    if (offgrid_row(md, tl, params, ln, u, q) && t < q.np)
+      wv[u] = *reinterpret_cast<const u32x4_t*>(q.base + q.lo + q.c0 + 8 * t);
+  }
+}
+// staged O of W row r, column c: tile element (r, c) of a wide matrix,
+// (c, r) of a tall one
+__device__ __forceinline__ uint16_t staged_o(const uint16_t* S, bool trans, int r, int c) {
+  return trans ? S[stg(c, r) + (r & 3)] : S[stg(r, c) + (c & 3)];
+}
+template <int ROLE>
+__device__ __forceinline__ void offgrid_update(uint16_t* S, const MatDev& md, uint16_t* params,
+                                               const ApplyConsts& ak, int i0w, int j0w,
+                                               int elane, const u32x4_t* wv) {
+  const OffgridTile tl = offgrid_tile<ROLE>(md, i0w, j0w);
+  // the single parameters' loads before the pieces' stores (a load issued
+  // after a store waits for it); fully unrolled passes keep wv and w1 in
+  // registers
+  uint16_t w1[32];
+  {
+    const int ln = opaque_lane(elane), t = ln & 15;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      OffgridRow q;
+      int c;
+      if (offgrid_row(md, tl, params, ln, u, q) && offgrid_single(q, t, c)) w1[u] = q.base[q.lo + c];
+    }
+  }
+  {
+    const int ln = opaque_lane(elane), t = ln & 15;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      OffgridRow q;
+      if (!offgrid_row(md, tl, params, ln, u, q) || t >= q.np) continue;
+      const int c = q.c0 + 8 * t;
+      u32x4_t o;
+      if (!md.trans) {
+        o = stg_read8(S, q.r, c);
+      } else {
+        // a W row of a tall matrix is a staged column: one value per row
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          o[k] = static_cast<uint32_t>(staged_o(S, true, q.r, c + 2 * k)) |
+                 (static_cast<uint32_t>(staged_o(S, true, q.r, c + 2 * k + 1)) << 16);
+      }
+      *reinterpret_cast<u32x4_t*>(const_cast<uint16_t*>(q.base) + q.lo + c) = apply8(ak, wv[u], o);
+      // one slot at a time: the scheduler would otherwise hoist the LDS
+      // reads of every slot (up to 8 per piece) ahead of the first store
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  {
+    const int ln = opaque_lane(elane), t = ln & 15;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      OffgridRow q;
+      int c;
+      if (!offgrid_row(md, tl, params, ln, u, q) || !offgrid_single(q, t, c)) continue;
+      const float o = bf16_to_f32(staged_o(S, md.trans, q.r, c));
+      const_cast<uint16_t*>(q.base)[q.lo + c] = f32_to_bf16(apply_one(ak, bf16_to_f32(w1[u]), o));
+    }
+  }
 }
 
 // One 256x256 output tile: operand pipeline, MFMA main loop, epilogue.
@@ -488,7 +637,8 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
       Wm = g.params + md.off;
     }
   }
-  const bool w_rows = APPLY && to_w && !md.trans;
+  // (md.fuse == 2: W off the 8-element grid, O is staged as for X')
+  const bool w_rows = APPLY && to_w && md.fuse == 1 && !md.trans;
   u32x4_t apre[32];
   if constexpr (aterm) {
     const int pl = opaque_lane(lane);
@@ -632,7 +782,11 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 
   if constexpr (APPLY) {
     if (to_w) {
-      if (!md.trans) {
+      if (md.fuse == 2) {
+        u32x4_t wv[32];
+        offgrid_load<ROLE>(md, g.params, i0w, j0w, elane, wv);
+        offgrid_update<ROLE>(S, md, g.params, ak, i0w, j0w, elane, wv);
+      } else if (!md.trans) {
         // the staged tile holds W': row stores into W
 #pragma unroll 8
         for (int u = 0; u < 32; ++u) {

@@ -5,10 +5,12 @@ equal.  Both compute W' = fma(-step, O, decay * W) from the same bf16 O, so
 the fused path needs no tolerance of its own; the unfused path is checked
 against the oracle in test_gpu_parity.py.
 
-Matrices are fused when the NS and the params are bf16, the parameter
-buffer is 16-byte aligned and the matrix's offset and cols are multiples of
-8 (wide ones write W rows from the tile rows, tall ones through the
-transposed pass); the others, and the small matrices, keep the apply kernel.
+Every tiled matrix is fused when the NS and the params are bf16 and the
+parameter buffer is 16-byte aligned.  Wide matrices write W rows from the
+tile rows, tall ones through a transposed pass.  When a matrix's offset or
+cols are off the 8-element grid, its W rows are realigned: 16-byte pieces
+on the grid, the parameters before and after them one by one.  The small
+matrices keep the apply kernel.
 """
 
 import pytest
@@ -23,19 +25,19 @@ pytestmark = pytest.mark.gpu
 
 BF16 = torch.bfloat16
 
-# (rows, cols, fused if the offset is a multiple of 8)
+# (rows, cols, tiled): every tiled matrix takes the fused update
 SHAPES = [
     (256, 512, True),     # wide, on the grid
     (520, 296, True),     # tall (transposed pass), cols % 8 == 0
-    (520, 300, False),    # tall, cols % 8 == 4
+    (520, 300, True),     # tall, cols % 8 == 4: realigned rows
     (700, 1000, True),    # wide, rows off the tile grid
     (1000, 776, True),    # tall, rows off the grid
-    (1000, 700, False),   # tall, cols % 8 == 4
+    (1000, 700, True),    # tall, cols % 8 == 4
     (129, 8, False),      # small-matrix path
     (64, 64, False),      # small-matrix path
     (2048, 5632, True),
     (5632, 2048, True),
-    (300, 520, True),     # offset made odd below: not fused
+    (300, 520, True),     # offset made odd below: realigned rows
     (330, 1024, True),    # wide, last tile row half padding (half-height tiles)
     (256, 1096, True),    # wide, last tile column half padding (half-width tiles)
 ]
@@ -47,7 +49,7 @@ def _layout(shapes, misalign=(10,)):
         if k in misalign:
             o += 3                         # an offset that is not a multiple of 8
         mats.append((o, r, c))
-        fused += int(f and o % 8 == 0)
+        fused += int(f)
         o += r * c
         o = (o + 7) // 8 * 8 + 8           # next offset aligned (gaps stay untouched)
     return mats, o + 8, fused
@@ -71,7 +73,7 @@ def test_fused_step_is_bitwise_the_apply_kernel(gpu, coef):
     mats, n, n_fused = _layout(SHAPES)
     a = Case(gpu, mats, n, 5)
     b = Case(gpu, mats, n, 5)
-    assert a.plan.info().fused_apply_mats == n_fused == 8
+    assert a.plan.info().fused_apply_mats == n_fused == 11
     hp = mhp(coef)
     p0 = a.params.clone()
     for _ in range(2):  # the second step starts from a nonzero momentum
@@ -81,6 +83,63 @@ def test_fused_step_is_bitwise_the_apply_kernel(gpu, coef):
     assert torch.equal(a.params.view(torch.int16), b.params.view(torch.int16))
     assert torch.equal(a.mom, b.mom)
     assert not torch.equal(a.params, p0)
+
+
+# every offset off the 8-element grid (odd shifts 1, 3, 5, 7 in turn), so
+# each W row starts at a different position within a 16-byte piece
+OFFGRID = [
+    (330, 1100),    # wide: half-height and half-width edge tiles
+    (1100, 330),    # tall: the same, through the transposed pass
+    (333, 1031),    # wide, odd cols
+    (1031, 333),    # tall, odd cols
+    (257, 2307),    # wide, one row into a second tile row
+    (2307, 257),    # tall
+    (3, 40000),     # wide, 3 rows (tiled: 40000 columns)
+    (40000, 3),     # tall, 3 columns: every W row shorter than a piece
+    (1500, 1501),   # square-ish, several tiles per side
+]
+
+
+def _offgrid_layout():
+    mats, o = [], 16
+    for k, (r, c) in enumerate(OFFGRID):
+        o += 2 * (k % 4) + 1
+        mats.append((o, r, c))
+        o += r * c
+    return mats, o   # the last matrix ends the buffer
+
+
+@pytest.mark.parametrize("coef", [QUINTIC, CUBIC])
+def test_offgrid_rows_fused_bitwise_the_apply_kernel(gpu, coef):
+    mats, n = _offgrid_layout()
+    guard = 64
+    res = []
+    plan = M.muon_plan_create(mats, n, "bf16", "bf16", "bf16")
+    info = plan.info()
+    assert info.fused_apply_mats == len(mats) and info.small_mats == 0
+    ws = plan.alloc_workspace(gpu)
+    for fused in (True, False):
+        g = torch.Generator(device=gpu)
+        g.manual_seed(31)
+        # `guard` elements past the buffer, which ends with the last matrix
+        base = (torch.randn(n + guard, generator=g, device=gpu) * 0.02).to(BF16)
+        grads = (torch.randn(n, generator=g, device=gpu) * 0.02).to(BF16)
+        mom = torch.zeros(n, device=gpu)
+        out = None if fused else torch.zeros(n, device=gpu)
+        p0 = base.clone()
+        for _ in range(2):
+            M.muon_step(plan, base[:n], grads, mom, ws, mhp(coef), out)
+        torch.cuda.synchronize()
+        # the gaps between matrices and the elements past the buffer are
+        # untouched; every matrix changed
+        covered = torch.zeros(n + guard, dtype=torch.bool, device=gpu)
+        for o, r, c in mats:
+            covered[o:o + r * c] = True
+            assert not torch.equal(base[o:o + r * c], p0[o:o + r * c])
+        assert torch.equal(base[~covered].view(torch.int16), p0[~covered].view(torch.int16))
+        res.append((base.view(torch.int16).clone(), mom.clone()))
+    assert torch.equal(res[0][0], res[1][0])
+    assert torch.equal(res[0][1], res[1][1])
 
 
 @pytest.mark.parametrize("steps", [0, 1, 2])

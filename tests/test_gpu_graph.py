@@ -21,8 +21,9 @@ pytestmark = pytest.mark.gpu
 
 class State:
     def __init__(self, gpu, seed):
-        # offsets on 8-element boundaries: (300, 520) and (520, 296) can take
-        # the fused update, (520, 300) cannot (cols % 8 != 0)
+        # offsets on 8-element boundaries: the tiled (300, 520), (520, 300)
+        # and (520, 296) take the fused update, (520, 300) with its rows
+        # realigned onto the 8-element grid (cols % 8 != 0)
         mats, o = [], 8
         for r, c in [(128, 256), (96, 200), (300, 520), (520, 300), (64, 64), (520, 296)]:
             mats.append((o, r, c))
@@ -58,7 +59,7 @@ def test_captured_step_replays_bitwise(gpu, with_out):
     hp, ahp = mhp(QUINTIC), W.AdamWHParams()
     eager = State(gpu, 21)
     assert eager.s.plan.info().small_mats == 3
-    assert eager.s.plan.info().fused_apply_mats == 2
+    assert eager.s.plan.info().fused_apply_mats == 3
     ref = []
     for _ in range(3):
         eager.step(hp, ahp, with_out)
