@@ -816,16 +816,20 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
       uint16_t* Sjq = S + efrow * 128 + ((((bj * 8 + 2 * q) ^ gacc) & 31) << 2);
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
+        // every rounding step as written (the small-matrix kernel computes
+        // the same expressions and must give the same bits)
+#pragma clang fp contract(off)
         u32x2_t* slotp = reinterpret_cast<u32x2_t*>(Sjq + bi * 32 * 128);
         f32x4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = sc * acc[bj][bi][4 * q + e];
         if constexpr (aterm) {
+          // fma(b, a, c A A), as in the small-matrix kernel
           const u32x2_t a0 = *slotp;
-          v[0] += g.b * lo_bf(a0[0]);
-          v[1] += g.b * hi_bf(a0[0]);
-          v[2] += g.b * lo_bf(a0[1]);
-          v[3] += g.b * hi_bf(a0[1]);
+          v[0] = fmaf(g.b, lo_bf(a0[0]), v[0]);
+          v[1] = fmaf(g.b, hi_bf(a0[0]), v[1]);
+          v[2] = fmaf(g.b, lo_bf(a0[1]), v[2]);
+          v[3] = fmaf(g.b, hi_bf(a0[1]), v[3]);
         }
         if (PHASE != 3 && bi == bj) {
 #pragma unroll

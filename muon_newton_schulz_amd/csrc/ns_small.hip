@@ -104,16 +104,19 @@ __device__ __forceinline__ void small_nt(const uint16_t* P, int ld, int K, int n
         const int i = bi * 32 + frow;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          // every rounding step as written, as in the tiled engine
+#pragma clang fp contract(off)
           const int j0 = bj * 32 + 8 * q + 4 * (lane >> 5);
           float x[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) x[e] = sc * acc[u][v][4 * q + e];
           if constexpr (ATERM) {
+            // fma(b, a, c A A), as the tiled engine writes it out
             const u32x2_t a = *reinterpret_cast<const u32x2_t*>(A + i * ldc + j0);
-            x[0] += bterm * lo_bf(a[0]);
-            x[1] += bterm * hi_bf(a[0]);
-            x[2] += bterm * lo_bf(a[1]);
-            x[3] += bterm * hi_bf(a[1]);
+            x[0] = fmaf(bterm, lo_bf(a[0]), x[0]);
+            x[1] = fmaf(bterm, hi_bf(a[0]), x[1]);
+            x[2] = fmaf(bterm, lo_bf(a[1]), x[2]);
+            x[3] = fmaf(bterm, hi_bf(a[1]), x[3]);
           }
           if (bi == bj) {
 #pragma unroll
