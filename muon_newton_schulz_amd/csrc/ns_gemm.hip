@@ -170,45 +170,6 @@ __device__ __forceinline__ void wait_lds16(s16x4_t* t) {
                : "memory");
 }
 
-// Partial waits: at most N LDS reads outstanding, tied to the fragments
-// the next MFMAs need (P fragments and one Q block; phase 3's Q block as
-// its two transposed halves).
-template <int N>
-__device__ __forceinline__ void wait_p4q1(bf16x8_t* p, bf16x8_t& q) {
-  asm volatile("s_waitcnt lgkmcnt(%5)"
-               : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(q)
-               : "n"(N)
-               : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_q1(bf16x8_t& q) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(q) : "n"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_p4t2(bf16x8_t* p, s16x4_t* t) {
-  asm volatile("s_waitcnt lgkmcnt(%6)"
-               : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(t[0]), "+v"(t[1])
-               : "n"(N)
-               : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_t2(s16x4_t* t) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(t[0]), "+v"(t[1]) : "n"(N) : "memory");
-}
-
-// Issue slot (after MFMA m of a stage's second group) of the next stage's
-// read j: in index order (P fragments, then Q block by block) on the odd
-// slots, and phase 3's four further reads on slots 8..11.
-__host__ __device__ constexpr int next_read_slot(int nr, int j) {
-  return nr == 8 || j < 4 ? 2 * j + 1
-         : j == 4         ? 8
-         : j <= 6         ? 9
-         : j == 7         ? 10
-         : j <= 9         ? 11
-         : j == 10        ? 13
-                          : 15;
-}
-
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
@@ -487,12 +448,6 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
   // per-lane byte offset within a ring slot (below) + the wave-uniform slot
   // base + an immediate.
   constexpr int NR = PHASE == 3 ? 12 : 8;
-  // Phase 3's whole tiles wait for each Q block's fragments just before
-  // its MFMAs (split roles, which read fewer fragments, wait for the whole
-  // set).  Phase 3 reads its next-stage fragments on slots up to the last
-  // MFMA of a stage, so its first block's wait had exposed an LDS latency;
-  // phases 1 and 2 gained nothing from it (dense phase 2 lost 2%).
-  constexpr bool PROG = PHASE == 3 && ROLE == 0;
   constexpr uint32_t SLOT_BYTES = 2 * BT * BK * 2;
   const uint32_t lds0 = lds_addr(smem);
   uint32_t vp[2], vq[2];  // K-contiguous fragments of k substep ks
@@ -623,28 +578,10 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
     constexpr bool REFILL = decltype(refill_c)::value;
     constexpr bool NEXT = decltype(next_c)::value;
     const uint32_t sb = lds0 + (kt % NSLOT) * SLOT_BYTES;
-    if constexpr (!PROG) settle(F[0]);
+    settle(F[0]);
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, 16>([&](auto m_c) {
       constexpr int m = decltype(m_c)::value;
-      if constexpr (PROG && (m & 3) == 0) {
-        // block bj = m / 4 needs Q fragment bj (and, first, the P
-        // fragments): the reads of F[0] went out in index order, and
-        // those of F[1] after MFMAs 0..m-1 of this group
-        constexpr int bj = m >> 2;
-        if constexpr (PHASE == 3) {
-          constexpr int N = (6 - 2 * bj) + (m < NR ? m : NR);
-          if constexpr (bj == 0) wait_p4t2<N>(F[0].p, F[0].t);
-          else wait_t2<N>(F[0].t + 2 * bj);
-          F[0].q[bj] = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(F[0].t[2 * bj], F[0].t[2 * bj + 1], 0, 1, 2, 3, 4,
-                                                5, 6, 7));
-        } else {
-          constexpr int N = (3 - bj) + (m < NR ? m : NR);
-          if constexpr (bj == 0) wait_p4q1<N>(F[0].p, F[0].q[0]);
-          else wait_q1<N>(F[0].q[bj]);
-        }
-      }
       if constexpr ((MASK >> m) & 1u)
         acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             F[0].q[m >> 2], F[0].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
@@ -666,14 +603,11 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
       if constexpr ((MASK >> m) & 1u)
         acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             F[1].q[m >> 2], F[1].p[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
-      // after MFMA m: DMA m/2 on even m, next-stage reads on odd m (and
-      // phase 3's further four on m = 8..11), in index order
+      // after MFMA m: DMA m/2 on even m, read m/2 on odd m, and reads
+      // 8..NR-1 after MFMAs 8..NR-1
       if constexpr (REFILL && (m & 1) == 0) issue_dma(kt + NSLOT - 1, rslot, Int<(m >> 1)>{});
-      if constexpr (NEXT)
-        static_for<0, NR>([&](auto j_c) {
-          constexpr int j = decltype(j_c)::value;
-          if constexpr (next_read_slot(NR, j) == m) issue_read(F[0], nsb, Int<0>{}, j_c);
-        });
+      if constexpr (NEXT && (m & 1) == 1) issue_read(F[0], nsb, Int<0>{}, Int<(m >> 1)>{});
+      if constexpr (NEXT && m >= 8 && m < NR) issue_read(F[0], nsb, Int<0>{}, Int<m>{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
