@@ -38,7 +38,9 @@ inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 struct Wave {
   int mat_begin = 0, mat_end = 0;
   int64_t k1_begin = 0, k1_count = 0;      // into the k1 item table
-  int64_t syrk_begin = 0, syrk_count = 0;  // phases 1 and 2 share the list
+  int64_t syrk_begin = 0, syrk_count = 0;  // phase 1's tiles (X X^T)
+  int64_t aa_begin = 0, aa_count = 0;      // phase 2's: the same tiles (A A),
+                                           // dealt out for phase 2's costs
   int64_t bx_begin = 0, bx_count = 0;
   int64_t small_begin = 0, small_count = 0;  // into the small-matrix table
   int64_t k7_begin = 0, k7_count = 0;  // elementwise tiles of the matrices whose
@@ -97,17 +99,18 @@ struct muon_plan {
   int tile = 0;
   size_t ws_bytes = 0;
   std::vector<MatDev> mats;
-  std::vector<Item> k1_items, syrk_items, bx_items, k7_items;
+  std::vector<Item> k1_items, syrk_items, aa_items, bx_items, k7_items;
   std::vector<int32_t> small_list;  // matrices run by the fused small-matrix kernel
   std::vector<Wave> waves;
   // the tables packed as the device sees them (built at creation; copied
   // into the caller's buffer by muon_plan_upload) and their byte offsets
   std::vector<char> host_tables;
-  size_t o_k1 = 0, o_syrk = 0, o_bx = 0, o_small = 0, o_k7 = 0;
+  size_t o_k1 = 0, o_syrk = 0, o_aa = 0, o_bx = 0, o_small = 0, o_k7 = 0;
   // device copies, inside the caller's table buffer
   MatDev* d_mats = nullptr;
   Item* d_k1 = nullptr;
   Item* d_syrk = nullptr;
+  Item* d_aa = nullptr;
   Item* d_bx = nullptr;
   Item* d_k7 = nullptr;
   int32_t* d_small = nullptr;
@@ -132,24 +135,69 @@ int64_t matrix_ws_elems(const MatDev& m) {
 // panels should therefore run on the same XCD at the same time: the
 // logical list is cut into groups of kGroup tiles (one group ~ the 32 CUs
 // of an XCD), group s goes to XCD s % 8, and within an XCD the groups run
-// in logical order.  The list is padded with empty items (mat = -1) to a
-// multiple of 8 * kGroup; those workgroups exit at once.
+// in logical order, one per round of the persistent tile walk (workgroup
+// b takes items b, b + 256, ...).  The list is padded with empty items
+// (mat = -1) to a multiple of 8 * kGroup; those workgroups skip them.
+//
+// Tiles differ in cost (K, split diagonal and half edge tiles), and with a
+// fixed lane per workgroup the differences would add up over the rounds:
+// the workgroups of an XCD would drift apart by whole tiles, each would
+// read its operand panels alone, and the panels would no longer be shared
+// in L2.  So each group's tiles are dealt out longest first to the
+// workgroups of its XCD that have the least estimated work so far (stable
+// in both orders, so that tiles of equal cost keep the plain mapping).
 constexpr int kXcds = 8;
 constexpr int kGroup = 32;
 constexpr int kSuperRows = 4, kSuperCols = 8;
 
-std::vector<Item> xcd_dispatch_order(const std::vector<Item>& logical) {
+template <typename Cost>
+std::vector<Item> xcd_dispatch_order(const std::vector<Item>& logical, Cost cost) {
   const int64_t n = static_cast<int64_t>(logical.size());
   if (n == 0) return {};
   const int64_t round = static_cast<int64_t>(kXcds) * kGroup;
   const int64_t padded = (n + round - 1) / round * round;
   std::vector<Item> out(static_cast<size_t>(padded), Item{-1, 0});
-  for (int64_t b = 0; b < padded; ++b) {
-    const int64_t x = b % kXcds, l = b / kXcds;
-    const int64_t li = ((l / kGroup) * kXcds + x) * kGroup + (l % kGroup);
-    if (li < n) out[static_cast<size_t>(b)] = logical[static_cast<size_t>(li)];
+  std::vector<double> work(static_cast<size_t>(kXcds) * kGroup, 0.0);
+  int tile_of[kGroup], lane_of[kGroup];
+  double c[kGroup];
+  for (int64_t g = 0; g * kGroup < n; ++g) {
+    const int64_t x = g % kXcds, rr = g / kXcds;
+    const int nt = static_cast<int>(std::min<int64_t>(kGroup, n - g * kGroup));
+    double* wx = work.data() + x * kGroup;
+    for (int t = 0; t < nt; ++t) {
+      tile_of[t] = t;
+      c[t] = cost(logical[static_cast<size_t>(g * kGroup + t)]);
+    }
+    for (int l = 0; l < kGroup; ++l) lane_of[l] = l;
+    std::stable_sort(tile_of, tile_of + nt, [&](int a, int b) { return c[a] > c[b]; });
+    std::stable_sort(lane_of, lane_of + kGroup, [&](int a, int b) { return wx[a] < wx[b]; });
+    for (int k = 0; k < nt; ++k) {
+      const int t = tile_of[k], l = lane_of[k];
+      out[static_cast<size_t>((rr * kGroup + l) * kXcds + x)] =
+          logical[static_cast<size_t>(g * kGroup + t)];
+      wx[l] += c[t];
+    }
   }
   return out;
+}
+
+// Estimated cost of a tile of NS phase `phase`, in K stages: the stages of
+// its main loop, scaled for the split roles (a split diagonal tile's
+// busiest wave does 10 of 16 MFMA blocks, a half edge tile 8), plus the
+// prologue and epilogue (about 13, 17 and 8 stages in phases 1, 2 and 3).
+// It only orders work: any value gives the same results.
+double tile_cost(const MatDev& d, int phase, const Item& it, int T) {
+  const int ti = static_cast<int>(it.rc >> 16), tj = static_cast<int>(it.rc & 0xffffu);
+  const double stages = (phase == 1 ? d.n_k : d.m_k) / static_cast<double>(muon::kNsKStep);
+  double f = 1.0;
+  if (d.split) {
+    const int m = std::min(d.rows, d.cols), n = std::max(d.rows, d.cols);
+    if (phase != 3 && ti == tj) f = 0.625;
+    else if (d.m_pad <= muon::kDiagInPlaceMaxTiles * T &&
+             ((phase == 3 && m - ti * T <= T / 2) || (phase == 3 ? n : m) - tj * T <= T / 2))
+      f = 0.5;
+  }
+  return stages * f + (phase == 1 ? 13.0 : phase == 2 ? 17.0 : 8.0);
 }
 
 // Launch order of an elementwise tile list: workgroup b runs on XCD b % 8,
@@ -350,9 +398,12 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     w.bytes = off;
     ws_max = std::max(ws_max, off);
 
-    // GEMM tile lists: matrices with the longest K first, each matrix's
-    // tiles in super-tile order, then permuted so that every XCD receives
-    // whole groups of neighbouring tiles (see xcd_dispatch_order).
+    // GEMM tile lists: each matrix's tiles in super-tile order, then
+    // permuted so that every XCD receives whole groups of neighbouring
+    // tiles (see xcd_dispatch_order).  Phases 1 and 2 (upper triangle of
+    // m x m, K = n and m) take the matrices by m, then n, descending, so
+    // that a group's tiles have much the same triangle and K; phase 3 by m
+    // (its K).  Large tiles first, small ones last, for the tail.
     std::vector<int> order;
     w.small_begin = static_cast<int64_t>(p.small_list.size());
     for (int m = w.mat_begin; m < w.mat_end; ++m) {
@@ -362,7 +413,8 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     w.small_count = static_cast<int64_t>(p.small_list.size()) - w.small_begin;
     std::vector<Item> syrk_l, bx_l;
     std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
-      return p.mats[x].n_pad > p.mats[y].n_pad;
+      const MatDev &a = p.mats[x], &b = p.mats[y];
+      return a.m_pad != b.m_pad ? a.m_pad > b.m_pad : a.n_pad > b.n_pad;
     });
     for (int m : order) emit_super_tiles(m, p.mats[m].m_pad / T, p.mats[m].m_pad / T, true, syrk_l);
     // the split diagonal tiles of large matrices after all off-diagonal tiles
@@ -375,11 +427,18 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
       return p.mats[x].m_pad > p.mats[y].m_pad;
     });
     for (int m : order) emit_super_tiles(m, p.mats[m].m_pad / T, p.mats[m].n_pad / T, false, bx_l);
-    const std::vector<Item> syrk = xcd_dispatch_order(syrk_l);
-    const std::vector<Item> bx = xcd_dispatch_order(bx_l);
+    auto cost_of = [&](int phase) {
+      return [&p, phase, T](const Item& it) { return tile_cost(p.mats[it.mat], phase, it, T); };
+    };
+    const std::vector<Item> syrk = xcd_dispatch_order(syrk_l, cost_of(1));
+    const std::vector<Item> aa = xcd_dispatch_order(syrk_l, cost_of(2));
+    const std::vector<Item> bx = xcd_dispatch_order(bx_l, [](const Item&) { return 1.0; });
     w.syrk_begin = static_cast<int64_t>(p.syrk_items.size());
     w.syrk_count = static_cast<int64_t>(syrk.size());
     p.syrk_items.insert(p.syrk_items.end(), syrk.begin(), syrk.end());
+    w.aa_begin = static_cast<int64_t>(p.aa_items.size());
+    w.aa_count = static_cast<int64_t>(aa.size());
+    p.aa_items.insert(p.aa_items.end(), aa.begin(), aa.end());
     w.bx_begin = static_cast<int64_t>(p.bx_items.size());
     w.bx_count = static_cast<int64_t>(bx.size());
     p.bx_items.insert(p.bx_items.end(), bx.begin(), bx.end());
@@ -396,12 +455,14 @@ void pack_tables(muon_plan& p) {
   const size_t b_mats = align_up(p.mats.size() * sizeof(MatDev), kAlign);
   const size_t b_k1 = align_up(p.k1_items.size() * sizeof(Item), kAlign);
   const size_t b_syrk = align_up(p.syrk_items.size() * sizeof(Item), kAlign);
+  const size_t b_aa = align_up(p.aa_items.size() * sizeof(Item), kAlign);
   const size_t b_bx = align_up(p.bx_items.size() * sizeof(Item), kAlign);
   const size_t b_small = align_up(p.small_list.size() * sizeof(int32_t), kAlign);
   const size_t b_k7 = align_up(p.k7_items.size() * sizeof(Item), kAlign);
   p.o_k1 = b_mats;
   p.o_syrk = p.o_k1 + b_k1;
-  p.o_bx = p.o_syrk + b_syrk;
+  p.o_aa = p.o_syrk + b_syrk;
+  p.o_bx = p.o_aa + b_aa;
   p.o_small = p.o_bx + b_bx;
   p.o_k7 = p.o_small + b_small;
   p.host_tables.assign(p.o_k7 + b_k7, 0);
@@ -412,6 +473,7 @@ void pack_tables(muon_plan& p) {
   put(0, p.mats.data(), p.mats.size() * sizeof(MatDev));
   put(p.o_k1, p.k1_items.data(), p.k1_items.size() * sizeof(Item));
   put(p.o_syrk, p.syrk_items.data(), p.syrk_items.size() * sizeof(Item));
+  put(p.o_aa, p.aa_items.data(), p.aa_items.size() * sizeof(Item));
   put(p.o_bx, p.bx_items.data(), p.bx_items.size() * sizeof(Item));
   put(p.o_small, p.small_list.data(), p.small_list.size() * sizeof(int32_t));
   put(p.o_k7, p.k7_items.data(), p.k7_items.size() * sizeof(Item));
@@ -584,6 +646,7 @@ int muon_plan_upload(muon_plan_t* plan, void* tables, size_t table_bytes, hipStr
   plan->d_mats = reinterpret_cast<MatDev*>(base);
   plan->d_k1 = reinterpret_cast<Item*>(base + plan->o_k1);
   plan->d_syrk = reinterpret_cast<Item*>(base + plan->o_syrk);
+  plan->d_aa = reinterpret_cast<Item*>(base + plan->o_aa);
   plan->d_bx = reinterpret_cast<Item*>(base + plan->o_bx);
   plan->d_small = reinterpret_cast<int32_t*>(base + plan->o_small);
   plan->d_k7 = reinterpret_cast<Item*>(base + plan->o_k7);
@@ -652,8 +715,10 @@ int run_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
                  const muon_hparams_t* hp, int32_t iter, int32_t phase, int32_t small_iters,
                  hipStream_t stream, void* fused_params = nullptr) {
   const Wave& w = plan->waves[wave];
-  const Item* items = phase == 3 ? plan->d_bx + w.bx_begin : plan->d_syrk + w.syrk_begin;
-  const int n = static_cast<int>(phase == 3 ? w.bx_count : w.syrk_count);
+  const Item* items = phase == 3   ? plan->d_bx + w.bx_begin
+                      : phase == 2 ? plan->d_aa + w.aa_begin
+                                   : plan->d_syrk + w.syrk_begin;
+  const int n = static_cast<int>(phase == 3 ? w.bx_count : phase == 2 ? w.aa_count : w.syrk_count);
   muon::GemmArgs g = gemm_args(plan, w, workspace, hp, iter, items);
   g.n_items = n;
   if (fused_params != nullptr) {
