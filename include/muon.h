@@ -161,7 +161,11 @@ typedef struct {
                                  all of them unless MUON_PLAN_WHOLE_TILES) */
   int32_t fused_apply_mats;   /* matrices whose update can be applied by the
                                  last phase 3 (muon_stage_ns_apply) */
-  int32_t reserved;
+  int32_t round_sync_phases;  /* bit p-1 set (p = 1, 2): the bf16 kernels of
+                                 NS phase p hold the tile rounds of each XCD
+                                 together (in at least one wave); a
+                                 scheduling choice of the plan, results do
+                                 not depend on it */
 } muon_plan_info_t;
 
 /* Host-only sizing: validates exactly as muon_plan_create and returns the
@@ -193,10 +197,21 @@ int muon_plan_create(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_num
  * mirrors the rest; for a matrix whose short side pads to more than 8 tiles
  * (2048) those tiles run after all off-diagonal tiles of the phase.  On a
  * matrix of at most 8 tiles per side, an edge tile whose last 128 rows or
- * columns are padding computes only the half that holds data.  The result is bitwise the same either way;
- * MUON_PLAN_WHOLE_TILES computes every tile whole, in place. */
+ * columns are padding computes only the half that holds data.  The result
+ * is bitwise the same either way; MUON_PLAN_WHOLE_TILES computes every tile
+ * whole, in place.
+ *
+ * The bf16 NS kernels keep one workgroup per CU walking the tile list in
+ * rounds of 32 tiles per XCD; tiles of a round share operand panels in the
+ * XCD's L2.  Where the plan finds that a round's tiles cost much the same
+ * (muon_plan_info_t.round_sync_phases), phases 1 and 2 hold each XCD's
+ * workgroups together every few rounds: a bounded wait on a counter in the
+ * workspace, a timing device only.  MUON_PLAN_FREE_ROUNDS turns it off
+ * (useful when other kernels share the GPU, where the wait runs into its
+ * bound); the result is bitwise the same either way. */
 #define MUON_PLAN_TILED_ONLY 1u
 #define MUON_PLAN_WHOLE_TILES 2u
+#define MUON_PLAN_FREE_ROUNDS 4u
 int muon_plan_create_ex(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                         int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype,
                         size_t workspace_cap, uint32_t flags, muon_plan_t** out,

@@ -105,7 +105,7 @@ class MuonPlanInfo(ctypes.Structure):
                 ("bx_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("ns_flops_per_iter_alg", ctypes.c_double), ("small_mats", ctypes.c_int32),
                 ("split_tile_mats", ctypes.c_int32), ("fused_apply_mats", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("round_sync_phases", ctypes.c_int32)]
 
 
 _lib_handle = None
@@ -330,14 +330,17 @@ def muon_workspace_size(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype
 
 MUON_PLAN_TILED_ONLY = 1
 MUON_PLAN_WHOLE_TILES = 2
+MUON_PLAN_FREE_ROUNDS = 4
 
 
 def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="bf16",
                      workspace_cap: int = 0, tiled_only: bool = False,
-                     whole_tiles: bool = False, upload: bool = True) -> MuonPlan:
+                     whole_tiles: bool = False, free_rounds: bool = False,
+                     upload: bool = True) -> MuonPlan:
     """tiled_only: every matrix on the tiled NS path (no fused small-matrix
     kernel); whole_tiles: every NS tile computed whole (no split diagonal
-    or edge tiles).  Results are bitwise the same either way.
+    or edge tiles); free_rounds: the NS kernels never hold an XCD's tile
+    rounds together.  Results are bitwise the same either way.
     upload: copy the tables to a new device tensor on torch's current device
     and stream (MuonPlan.upload); without it the plan stays host-only."""
     arr = _mats_array(mats)
@@ -347,7 +350,8 @@ def muon_plan_create(mats, flat_numel: int, param_dtype, grad_dtype, ns_dtype="b
                                      dtype_code(grad_dtype), dtype_code(ns_dtype),
                                      int(workspace_cap),
                                      (MUON_PLAN_TILED_ONLY if tiled_only else 0)
-                                     | (MUON_PLAN_WHOLE_TILES if whole_tiles else 0),
+                                     | (MUON_PLAN_WHOLE_TILES if whole_tiles else 0)
+                                     | (MUON_PLAN_FREE_ROUNDS if free_rounds else 0),
                                      ctypes.byref(h), ctypes.byref(ws)))
     plan = MuonPlan(h.value, ws.value, len(mats), int(flat_numel), dtype_code(param_dtype),
                     dtype_code(grad_dtype))

@@ -45,7 +45,8 @@ struct Wave {
   int64_t small_begin = 0, small_count = 0;  // into the small-matrix table
   int64_t k7_begin = 0, k7_count = 0;  // elementwise tiles of the matrices whose
                                        // update is not fused into phase 3
-  size_t partial_off = 0, norm_off = 0, inv_off = 0;  // byte offsets in the workspace
+  size_t partial_off = 0, norm_off = 0, inv_off = 0, sync_off = 0;  // byte offsets in the workspace
+  bool sync[2] = {false, false};  // NS phases 1, 2 hold each XCD's rounds together
   size_t bytes = 0;
 };
 
@@ -181,6 +182,39 @@ std::vector<Item> xcd_dispatch_order(const std::vector<Item>& logical, Cost cost
   return out;
 }
 
+// Whether the round barrier pays for a dispatched list: the relative
+// increase of the estimated makespan when every kSyncEvery-th round of an
+// XCD starts only after the slowest of its workgroups has finished the
+// previous one.
+// The barrier keeps the workgroups that share operand panels in step (they
+// then read them from L2); it is worth its idle time only where a round's
+// tiles cost much the same.
+template <typename Cost>
+double barrier_idle(const std::vector<Item>& dispatched, Cost cost) {
+  const int64_t n = static_cast<int64_t>(dispatched.size());
+  const int64_t round = static_cast<int64_t>(kXcds) * kGroup;
+  if (n <= round) return 0.0;
+  std::vector<double> free_run(static_cast<size_t>(round), 0.0), synced(free_run);
+  for (int64_t r = 0; r * round < n; ++r) {
+    for (int x = 0; x < kXcds && r % muon::kSyncEvery == 0; ++x) {
+      double mx = 0.0;
+      for (int l = 0; l < kGroup; ++l) mx = std::max(mx, synced[static_cast<size_t>(l * kXcds + x)]);
+      for (int l = 0; l < kGroup; ++l) synced[static_cast<size_t>(l * kXcds + x)] = mx;
+    }
+    for (int64_t b = 0; b < round && r * round + b < n; ++b) {
+      const Item& it = dispatched[static_cast<size_t>(r * round + b)];
+      if (it.mat < 0) continue;
+      const double c = cost(it);
+      free_run[static_cast<size_t>(b)] += c;
+      synced[static_cast<size_t>(b)] += c;
+    }
+  }
+  const double a = *std::max_element(free_run.begin(), free_run.end());
+  const double s = *std::max_element(synced.begin(), synced.end());
+  return a > 0.0 ? s / a - 1.0 : 0.0;
+}
+constexpr double kBarrierMaxIdle = 0.01;
+
 // Estimated cost of a tile of NS phase `phase`, in K stages: the stages of
 // its main loop, scaled for the split roles (a split diagonal tile's
 // busiest wave does 10 of 16 MFMA blocks, a half edge tile 8), plus the
@@ -193,7 +227,7 @@ double tile_cost(const MatDev& d, int phase, const Item& it, int T) {
   if (d.split) {
     const int m = std::min(d.rows, d.cols), n = std::max(d.rows, d.cols);
     if (phase != 3 && ti == tj) f = 0.625;
-    else if (d.m_pad <= muon::kDiagInPlaceMaxTiles * T &&
+    else if (d.m_pad <= muon::kSplitEdgeMaxTiles * T &&
              ((phase == 3 && m - ti * T <= T / 2) || (phase == 3 ? n : m) - tj * T <= T / 2))
       f = 0.5;
   }
@@ -234,7 +268,8 @@ void emit_super_tiles(int mat, int rows, int cols, bool tri, std::vector<Item>& 
 int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
                int32_t param_dtype, int32_t grad_dtype, int32_t ns_dtype, size_t workspace_cap,
                uint32_t flags, muon_plan& p) {
-  if ((flags & ~static_cast<uint32_t>(MUON_PLAN_TILED_ONLY | MUON_PLAN_WHOLE_TILES)) != 0)
+  if ((flags & ~static_cast<uint32_t>(MUON_PLAN_TILED_ONLY | MUON_PLAN_WHOLE_TILES |
+                                      MUON_PLAN_FREE_ROUNDS)) != 0)
     return fail(MUON_ERR_INVALID_ARG, "unknown plan flags");
   if (n_mats < 0) return fail(MUON_ERR_INVALID_ARG, "n_mats < 0");
   if (n_mats > 0 && mats == nullptr) return fail(MUON_ERR_INVALID_ARG, "mats is null");
@@ -317,9 +352,9 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
   };
   auto fixed_bytes = [&](int64_t k1, int64_t nm) {
     // fp64 partial sums (one per k1 tile), fp32 norms and inverse norms
-    // (one per matrix)
+    // (one per matrix), the NS kernels' round counters
     return align_up(static_cast<size_t>(k1) * 8, kAlign) +
-           2 * align_up(static_cast<size_t>(nm) * 4, kAlign);
+           2 * align_up(static_cast<size_t>(nm) * 4, kAlign) + muon::kSyncBytes;
   };
   {
     int32_t i = 0;
@@ -395,15 +430,23 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
       const std::vector<Item> k1 = xcd_contiguous_order(k1_l);
       std::copy(k1.begin(), k1.end(), p.k1_items.begin() + w.k1_begin);
     }
+    // the NS kernels' round counters, after the matrices (which keep the
+    // same addresses with or without them)
+    w.sync_off = off;
+    off += muon::kSyncBytes;
     w.bytes = off;
     ws_max = std::max(ws_max, off);
 
     // GEMM tile lists: each matrix's tiles in super-tile order, then
     // permuted so that every XCD receives whole groups of neighbouring
-    // tiles (see xcd_dispatch_order).  Phases 1 and 2 (upper triangle of
-    // m x m, K = n and m) take the matrices by m, then n, descending, so
-    // that a group's tiles have much the same triangle and K; phase 3 by m
-    // (its K).  Large tiles first, small ones last, for the tail.
+    // tiles (see xcd_dispatch_order).  Phases 1 and 2 cover the upper
+    // triangle of m x m with K = n and K = m; each takes the matrices by
+    // its own K, then the other side, so that a round's tiles cost much
+    // the same.  Matrices with more than kSplitEdgeMaxTiles tiles per side
+    // run their split diagonal tiles after all off-diagonal tiles; smaller
+    // ones keep them in place, next to the tiles that share their panels.
+    // Phase 3 takes the matrices by m (its K).  Large tiles first, small
+    // ones last, for the tail.
     std::vector<int> order;
     w.small_begin = static_cast<int64_t>(p.small_list.size());
     for (int m = w.mat_begin; m < w.mat_end; ++m) {
@@ -411,18 +454,25 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
       else order.push_back(m);
     }
     w.small_count = static_cast<int64_t>(p.small_list.size()) - w.small_begin;
-    std::vector<Item> syrk_l, bx_l;
-    std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
-      const MatDev &a = p.mats[x], &b = p.mats[y];
-      return a.m_pad != b.m_pad ? a.m_pad > b.m_pad : a.n_pad > b.n_pad;
-    });
-    for (int m : order) emit_super_tiles(m, p.mats[m].m_pad / T, p.mats[m].m_pad / T, true, syrk_l);
-    // the split diagonal tiles of large matrices after all off-diagonal tiles
-    std::stable_partition(syrk_l.begin(), syrk_l.end(), [&](const Item& it) {
-      const MatDev& d = p.mats[it.mat];
-      return !(d.split && d.m_pad / T > muon::kDiagInPlaceMaxTiles &&
-               (it.rc >> 16) == (it.rc & 0xffffu));
-    });
+    auto triangle_list = [&](bool by_n) {
+      std::vector<int> o = order;
+      std::stable_sort(o.begin(), o.end(), [&](int x, int y) {
+        const MatDev &a = p.mats[x], &b = p.mats[y];
+        const int ka = by_n ? a.n_k : a.m_k, kb = by_n ? b.n_k : b.m_k;
+        if (ka != kb) return ka > kb;
+        return by_n ? a.m_pad > b.m_pad : a.n_pad > b.n_pad;
+      });
+      std::vector<Item> l;
+      for (int m : o) emit_super_tiles(m, p.mats[m].m_pad / T, p.mats[m].m_pad / T, true, l);
+      std::stable_partition(l.begin(), l.end(), [&](const Item& it) {
+        const MatDev& d = p.mats[it.mat];
+        return !(d.split && d.m_pad / T > muon::kSplitEdgeMaxTiles &&
+                 (it.rc >> 16) == (it.rc & 0xffffu));
+      });
+      return l;
+    };
+    const std::vector<Item> syrk_l = triangle_list(true), aa_l = triangle_list(false);
+    std::vector<Item> bx_l;
     std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
       return p.mats[x].m_pad > p.mats[y].m_pad;
     });
@@ -431,8 +481,21 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
       return [&p, phase, T](const Item& it) { return tile_cost(p.mats[it.mat], phase, it, T); };
     };
     const std::vector<Item> syrk = xcd_dispatch_order(syrk_l, cost_of(1));
-    const std::vector<Item> aa = xcd_dispatch_order(syrk_l, cost_of(2));
+    const std::vector<Item> aa = xcd_dispatch_order(aa_l, cost_of(2));
     const std::vector<Item> bx = xcd_dispatch_order(bx_l, [](const Item&) { return 1.0; });
+    // Phases 1 and 2 hold their rounds together where it costs little
+    // idle time (a list of at most kSyncEvery rounds is never held).
+    // Phase 3 never does: its workgroups stay within a few tens of K
+    // stages of each other without it (a workgroup that runs ahead takes
+    // the L2 misses), and the hold measured 0.5-2% slower there.
+    if (ns_dtype == MUON_DTYPE_BF16 && !(flags & MUON_PLAN_FREE_ROUNDS)) {
+      auto pays = [&](const std::vector<Item>& l, int phase) {
+        return static_cast<int64_t>(l.size()) > int64_t{muon::kSyncEvery} * kXcds * kGroup &&
+               barrier_idle(l, cost_of(phase)) <= kBarrierMaxIdle;
+      };
+      w.sync[0] = pays(syrk, 1);
+      w.sync[1] = pays(aa, 2);
+    }
     w.syrk_begin = static_cast<int64_t>(p.syrk_items.size());
     w.syrk_count = static_cast<int64_t>(syrk.size());
     p.syrk_items.insert(p.syrk_items.end(), syrk.begin(), syrk.end());
@@ -442,7 +505,8 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     w.bx_begin = static_cast<int64_t>(p.bx_items.size());
     w.bx_count = static_cast<int64_t>(bx.size());
     p.bx_items.insert(p.bx_items.end(), bx.begin(), bx.end());
-    if (w.k1_count > 0x7fffffff || w.syrk_count > 0x7fffffff || w.bx_count > 0x7fffffff)
+    if (w.k1_count > 0x7fffffff || w.syrk_count > 0x7fffffff || w.aa_count > 0x7fffffff ||
+        w.bx_count > 0x7fffffff)
       return fail(MUON_ERR_BAD_SHAPE, "too many tiles in one wave");
   }
   p.ws_bytes = ws_max;
@@ -532,6 +596,7 @@ muon::GemmArgs gemm_args(const muon_plan_t* p, const Wave& w, void* ws, const mu
   g.items = items;
   g.ws = ws;
   g.inv = reinterpret_cast<const float*>(ws_bytes_ptr(ws, w.inv_off));
+  g.sync = nullptr;  // set per phase by run_ns_phase
   g.a = hp->ns_a;
   g.b = hp->ns_b;
   g.c = hp->ns_c;
@@ -677,7 +742,9 @@ int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {
     info->split_tile_mats += d.split;
     info->fused_apply_mats += d.fuse != 0;
   }
-  info->reserved = 0;
+  info->round_sync_phases = 0;
+  for (const Wave& w : plan->waves)
+    for (int ph = 0; ph < 2; ++ph) info->round_sync_phases |= w.sync[ph] ? 1 << ph : 0;
   return MUON_OK;
 }
 
@@ -721,6 +788,8 @@ int run_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
   const int n = static_cast<int>(phase == 3 ? w.bx_count : phase == 2 ? w.aa_count : w.syrk_count);
   muon::GemmArgs g = gemm_args(plan, w, workspace, hp, iter, items);
   g.n_items = n;
+  if (phase != 3 && w.sync[phase - 1])
+    g.sync = reinterpret_cast<uint32_t*>(ws_bytes_ptr(workspace, w.sync_off));
   if (fused_params != nullptr) {
     g.params = static_cast<uint16_t*>(fused_params);
     g.clip = clip_of(hp->clip);

@@ -19,11 +19,17 @@ constexpr int kNsKStep = 32;  // bf16 engine: K per pipeline stage
 constexpr int kSmallM = 128;
 constexpr int kSmallElems = 32768;
 // Tiled bf16 NS: the diagonal tiles of A = X X^T and A A split their upper
-// blocks between the waves.  A matrix with more than this many tiles per
-// side of A (m_pad / kTileBf16) has its diagonal tiles run after every
-// off-diagonal tile of the phase; a smaller one keeps them in place, next
-// to the tiles that share their operand panels.
-constexpr int kDiagInPlaceMaxTiles = 8;
+// blocks between the waves, and a matrix with at most this many tiles per
+// side of A (m_pad / kTileBf16) also splits its half-empty edge tiles.
+constexpr int kSplitEdgeMaxTiles = 8;
+
+// Workspace area for the round counters of the persistent NS kernels: one
+// 32-bit counter per XCD group, 256 bytes apart.
+constexpr int kSyncGroups = 8;
+constexpr int kSyncStride = 64;  // uint32 elements
+constexpr size_t kSyncBytes = kSyncGroups * kSyncStride * 4;
+// rounds between two holds (each costs a device-scope atomic and polling)
+constexpr int kSyncEvery = 4;
 
 // Layout of the bf16 NS workspace.  Every matrix there (the iterates X,
 // A and B; all have m_pad rows) is stored as panels of 32 columns: panel q
@@ -105,6 +111,10 @@ struct GemmArgs {
   const ClipState* clip;  // guarded step (skip: W untouched), or null
   float lr, wd, rms_target;
   int32_t scale_mode;
+  // Round counters of the persistent bf16 kernels of phases 1 and 2, one
+  // per XCD group, kSyncStride apart; zeroed on the stream before each
+  // launch that uses them.
+  uint32_t* sync;
 };
 
 // kernel launchers (defined in the .hip files)

@@ -230,13 +230,13 @@ __device__ __forceinline__ u32x4_t stg_read8(const uint16_t* S, int i, int c) {
 // (ROLE 4: the Q side) are all padding: the four waves split the two
 // quadrants that hold data, 64 Q rows each, as ROLE 2 splits one, so the
 // tile costs 8 MFMA slots per substep; only on matrices with at most
-// kDiagInPlaceMaxTiles tiles per side (on larger ones they measured
+// kSplitEdgeMaxTiles tiles per side (on larger ones they measured
 // slower).  ROLE 0: the whole quadrant.  Only matrices with MatDev::split
 // take split tiles.
 __device__ __forceinline__ int tile_role(int phase, const MatDev& md, int ti, int tj, int wave) {
   if (!md.split) return 0;
   if (phase != 3 && ti == tj) return (wave == 0 || wave == 3) ? 1 : 2;
-  if (md.m_pad > kDiagInPlaceMaxTiles * BT) return 0;
+  if (md.m_pad > kSplitEdgeMaxTiles * BT) return 0;
   const int m = md.rows < md.cols ? md.rows : md.cols;
   const int n = md.rows < md.cols ? md.cols : md.rows;
   if (phase == 3 && m - ti * BT <= BT / 2) return 3;
@@ -905,13 +905,42 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 // their uniform loads become scalar loads, which do not wait for the
 // previous tile's stores (vector loads would: vmcnt counts loads and
 // stores together).
+//
+// With GemmArgs::sync set (phases 1 and 2, where the planner finds that a
+// round's tiles cost much the same) the walk also holds each XCD's
+// workgroups together: a workgroup that starts round r (its items are idx = b + r *
+// gridDim.x), r a multiple of kSyncEvery, first waits until the other
+// workgroups of its XCD group have finished round r - 1.  Without it they drift apart by whole tiles over
+// the rounds and read the shared operand panels at different times, from
+// HBM instead of L2.  The wait is a timing device only and is bounded:
+// after kSyncSpins polls the workgroup goes on (a member of the group may
+// not be resident while other kernels hold CUs).
+constexpr int kSyncSpins = 1024;
+__device__ __forceinline__ void xcd_round_barrier(uint32_t* cnt, uint32_t target) {
+  __syncthreads();  // every wave is done with the previous round
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < kSyncSpins; ++i) {
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
 template <int PHASE>
 __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g, const Item* __restrict__ items,
                                                     const MatDev* __restrict__ mats,
                                                     const float* __restrict__ invs) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * 2 * BT * BK];  // 128 KiB
   bool busy = false;
-  for (int idx = blockIdx.x; idx < g.n_items; idx += gridDim.x) {
+  uint32_t* const cnt =
+      g.sync != nullptr ? g.sync + (blockIdx.x % kSyncGroups) * kSyncStride : nullptr;
+  const uint32_t group = gridDim.x / kSyncGroups;
+  uint32_t round = 0;
+  for (int idx = blockIdx.x; idx < g.n_items; idx += gridDim.x, ++round) {
+    if (cnt != nullptr && round > 0 && round % kSyncEvery == 0)
+      xcd_round_barrier(cnt, group * (round / kSyncEvery));
     const Item it = items[idx];
     if (it.mat < 0) continue;  // padding of the XCD-grouped order
     const MatDev md = mats[it.mat];
@@ -1050,6 +1079,11 @@ __global__ __launch_bounds__(256) void k_ns_f32(GemmArgs g) {
   }
 }
 
+__global__ void k_zero_u32(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 }  // namespace
 
 hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
@@ -1058,15 +1092,26 @@ hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
   const dim3 block(256);
   if (ns_dtype == 1) {
     const dim3 grid(n_items < n_cu ? n_items : n_cu);
-    if (phase == 3 && args.params != nullptr)
-      hipLaunchKernelGGL(k_ns_bf16_apply, grid, block, 0, s, args, args.items, args.mats,
-                         args.inv);
+    // round counters (phases 1, 2): on a grid of whole 32-workgroup XCD
+    // groups with every workgroup walking the same number of rounds
+    GemmArgs a = args;
+    const bool sync = (phase == 1 || phase == 2) && a.sync != nullptr &&
+                      static_cast<int>(grid.x) == kSyncGroups * 32 && n_items > static_cast<int>(grid.x) &&
+                      n_items % static_cast<int>(grid.x) == 0;
+    if (sync) {
+      hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(kSyncGroups * kSyncStride), 0, s, a.sync,
+                         kSyncGroups * kSyncStride);
+    } else {
+      a.sync = nullptr;
+    }
+    if (phase == 3 && a.params != nullptr)
+      hipLaunchKernelGGL(k_ns_bf16_apply, grid, block, 0, s, a, a.items, a.mats, a.inv);
     else if (phase == 1)
-      hipLaunchKernelGGL(k_ns_bf16<1>, grid, block, 0, s, args, args.items, args.mats, args.inv);
+      hipLaunchKernelGGL(k_ns_bf16<1>, grid, block, 0, s, a, a.items, a.mats, a.inv);
     else if (phase == 2)
-      hipLaunchKernelGGL(k_ns_bf16<2>, grid, block, 0, s, args, args.items, args.mats, args.inv);
+      hipLaunchKernelGGL(k_ns_bf16<2>, grid, block, 0, s, a, a.items, a.mats, a.inv);
     else
-      hipLaunchKernelGGL(k_ns_bf16<3>, grid, block, 0, s, args, args.items, args.mats, args.inv);
+      hipLaunchKernelGGL(k_ns_bf16<3>, grid, block, 0, s, a, a.items, a.mats, a.inv);
   } else {
     const dim3 grid(n_items);
     if (phase == 1) hipLaunchKernelGGL(k_ns_f32<1>, grid, block, 0, s, args);

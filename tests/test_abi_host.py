@@ -63,13 +63,15 @@ def test_workspace_size_layout():
     # m_pad 256, n_pad 512; X ping-pong (2*256*512) and A, B (2*256*256), bf16.
     b = M.muon_workspace_size([(0, 300, 100)], 30000, "bf16", "bf16", "bf16")
     k1 = (512 // 64) * (256 // 64)
-    fixed = 256 + 256 + 256  # fp64 partials (k1*8 <= 256), norms, inverse norms
+    # fp64 partials (k1*8 <= 256), norms, inverse norms, and the NS
+    # kernels' round counters (8 groups x 256 bytes)
+    fixed = 256 + 256 + 256 + 2048
     assert k1 * 8 <= 256
     assert b == fixed + 2 * (2 * 256 * 512 + 2 * 256 * 256)
     # fp32 NS pads to 64: 128x256 -> X ping-pong and A, B in fp32
     b = M.muon_workspace_size([(0, 128, 256)], 128 * 256, "fp32", "fp32", "fp32")
     k1 = 2 * 4
-    assert b == 256 * 3 + 4 * (2 * 128 * 256 + 2 * 128 * 128)
+    assert b == 256 * 3 + 2048 + 4 * (2 * 128 * 256 + 2 * 128 * 128)
     # empty plan
     assert M.muon_workspace_size([], 0, "bf16", "bf16", "bf16") == 0
 
@@ -205,11 +207,13 @@ def test_plan_flags_validate_before_any_hip_call():
         return L.muon_plan_create_ex(mats, 1, 64, 1, 1, 1, 0, flags, ctypes.byref(h),
                                      ctypes.byref(ws))
     assert M.MUON_PLAN_TILED_ONLY == 1 and M.MUON_PLAN_WHOLE_TILES == 2
-    assert rc(4) == M.MUON_ERR_INVALID_ARG
+    assert M.MUON_PLAN_FREE_ROUNDS == 4
+    assert rc(8) == M.MUON_ERR_INVALID_ARG
     assert rc(1 << 31) == M.MUON_ERR_INVALID_ARG
-    # the known flags pass validation and the call gets as far as the device
-    for f in (0, 1, 2, 3):
-        assert rc(f) not in (M.MUON_ERR_INVALID_ARG, M.MUON_ERR_BAD_SHAPE, M.MUON_ERR_BAD_DTYPE)
+    # the known flags pass validation (creation is host-only)
+    for f in range(8):
+        assert rc(f) == M.MUON_OK
+        L.muon_plan_destroy(h)
 
 
 def test_longest_side_a_plan_accepts():
@@ -233,7 +237,7 @@ def test_stage_ns_apply_validates_before_any_hip_call():
         M.MUON_ERR_INVALID_ARG
     # plan info carries the count of matrices whose update the last NS phase applies
     names = [f[0] for f in M.MuonPlanInfo._fields_]
-    assert names[-2:] == ["fused_apply_mats", "reserved"]
+    assert names[-2:] == ["fused_apply_mats", "round_sync_phases"]
 
 
 def test_plans_are_host_only_until_uploaded():
@@ -301,3 +305,26 @@ def test_library_allocates_no_device_memory_and_never_synchronises():
     for f in SOURCES + ["muon_internal.h"]:
         text = re.sub(r"//[^\n]*", "", open(os.path.join(csrc, f)).read())
         assert not banned.search(text), (f, banned.search(text).group(0))
+
+
+def test_round_barrier_choice():
+    # Phases 1 and 2 hold each XCD's tile rounds together only where the
+    # plan's cost model predicts almost no idle time.  2048-sided matrices
+    # mix split diagonal tiles (10 of 16 MFMA blocks) into every round of
+    # the triangle, so they run free; larger ones run their diagonal tiles
+    # last, and their rounds are uniform.  Phase 3 never holds; neither does
+    # a list of at most 4 rounds of 256 tiles (the hold comes every 4th
+    # round), nor the fp32 engine.
+    def phases(mats, nsd="bf16"):
+        n = max(o + r * c for o, r, c in mats)
+        plan = M.muon_plan_create(mats, n, nsd, nsd, nsd, upload=False)
+        try:
+            return plan.info().round_sync_phases
+        finally:
+            plan.close()
+    sq = [(k * 2048 * 2048, 2048, 2048) for k in range(64)]
+    assert phases(sq) == 0
+    big = [(k * 4096 * 8192, 4096, 8192) for k in range(8)]
+    assert phases(big) == 0b11
+    assert phases(big[:7]) == 0         # 7 x 136 triangle tiles: 4 rounds
+    assert phases(big, "fp32") == 0

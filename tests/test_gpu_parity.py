@@ -60,7 +60,7 @@ class Setup:
 
     def __init__(self, mats, n, param_dtype, grad_dtype, ns_dtype, dev, seed=0,
                  w_std=1.0, g_std=1.0, cap=0, sentinel=True, tiled_only=False,
-                 whole_tiles=False):
+                 whole_tiles=False, free_rounds=False):
         self.mats, self.n = mats, n
         self.param_dtype, self.ns_dtype = param_dtype, ns_dtype
         g = torch.Generator(device=dev)
@@ -76,7 +76,8 @@ class Setup:
                 self.grads.dtype)
             self.mom[o:o + r * c] = 0.0
         self.plan = M.muon_plan_create(mats, n, param_dtype, grad_dtype, ns_dtype, cap,
-                                       tiled_only=tiled_only, whole_tiles=whole_tiles)
+                                       tiled_only=tiled_only, whole_tiles=whole_tiles,
+                                       free_rounds=free_rounds)
         self.ws = self.plan.alloc_workspace(dev)
         self.out = torch.full((n,), fill, dtype=torch.float32, device=dev)
 
