@@ -667,6 +667,8 @@ def main():
             "adamw_stream": args.adamw_stream,
             "adamw_beside_phase": args.adamw_beside if args.adamw_stream == "side" else None,
             "workspace_GiB": round(plan.workspace_bytes / 2 ** 30, 3),
+            # NS phases whose XCD tile rounds the plan holds together (bit p-1)
+            "round_sync_phases": info.round_sync_phases,
         },
         "value_definition": "algorithmic NS flops of one step / whole optimizer step time",
         "roofline": {

@@ -46,7 +46,8 @@ struct Wave {
   int64_t k7_begin = 0, k7_count = 0;  // elementwise tiles of the matrices whose
                                        // update is not fused into phase 3
   size_t partial_off = 0, norm_off = 0, inv_off = 0, sync_off = 0;  // byte offsets in the workspace
-  bool sync[2] = {false, false};  // NS phases 1, 2 hold each XCD's rounds together
+  // NS phases 1, 2: rounds between two holds of each XCD's workgroups (0: no hold)
+  int32_t sync_every[2] = {0, 0};
   size_t bytes = 0;
 };
 
@@ -183,20 +184,20 @@ std::vector<Item> xcd_dispatch_order(const std::vector<Item>& logical, Cost cost
 }
 
 // Whether the round barrier pays for a dispatched list: the relative
-// increase of the estimated makespan when every kSyncEvery-th round of an
+// increase of the estimated makespan when every `every`-th round of an
 // XCD starts only after the slowest of its workgroups has finished the
 // previous one.
 // The barrier keeps the workgroups that share operand panels in step (they
 // then read them from L2); it is worth its idle time only where a round's
 // tiles cost much the same.
 template <typename Cost>
-double barrier_idle(const std::vector<Item>& dispatched, Cost cost) {
+double barrier_idle(const std::vector<Item>& dispatched, Cost cost, int every) {
   const int64_t n = static_cast<int64_t>(dispatched.size());
   const int64_t round = static_cast<int64_t>(kXcds) * kGroup;
   if (n <= round) return 0.0;
   std::vector<double> free_run(static_cast<size_t>(round), 0.0), synced(free_run);
   for (int64_t r = 0; r * round < n; ++r) {
-    for (int x = 0; x < kXcds && r % muon::kSyncEvery == 0; ++x) {
+    for (int x = 0; x < kXcds && r % every == 0; ++x) {
       double mx = 0.0;
       for (int l = 0; l < kGroup; ++l) mx = std::max(mx, synced[static_cast<size_t>(l * kXcds + x)]);
       for (int l = 0; l < kGroup; ++l) synced[static_cast<size_t>(l * kXcds + x)] = mx;
@@ -484,17 +485,20 @@ int build_plan(const muon_matrix_t* mats, int32_t n_mats, int64_t flat_numel,
     const std::vector<Item> aa = xcd_dispatch_order(aa_l, cost_of(2));
     const std::vector<Item> bx = xcd_dispatch_order(bx_l, [](const Item&) { return 1.0; });
     // Phases 1 and 2 hold their rounds together where it costs little
-    // idle time (a list of at most kSyncEvery rounds is never held).
+    // idle time: every `every` rounds, the shortest period that does
+    // (a list of at most `every` rounds has no hold).
     // Phase 3 never does: its workgroups stay within a few tens of K
     // stages of each other without it (a workgroup that runs ahead takes
     // the L2 misses), and the hold measured 0.5-2% slower there.
     if (ns_dtype == MUON_DTYPE_BF16 && !(flags & MUON_PLAN_FREE_ROUNDS)) {
-      auto pays = [&](const std::vector<Item>& l, int phase) {
-        return static_cast<int64_t>(l.size()) > int64_t{muon::kSyncEvery} * kXcds * kGroup &&
-               barrier_idle(l, cost_of(phase)) <= kBarrierMaxIdle;
+      auto period = [&](const std::vector<Item>& l, int phase) {
+        const int64_t rounds = static_cast<int64_t>(l.size()) / (int64_t{kXcds} * kGroup);
+        for (int e = muon::kSyncEveryMin; e <= muon::kSyncEveryMax; e *= 2)
+          if (rounds > e && barrier_idle(l, cost_of(phase), e) <= kBarrierMaxIdle) return e;
+        return 0;
       };
-      w.sync[0] = pays(syrk, 1);
-      w.sync[1] = pays(aa, 2);
+      w.sync_every[0] = period(syrk, 1);
+      w.sync_every[1] = period(aa, 2);
     }
     w.syrk_begin = static_cast<int64_t>(p.syrk_items.size());
     w.syrk_count = static_cast<int64_t>(syrk.size());
@@ -597,6 +601,7 @@ muon::GemmArgs gemm_args(const muon_plan_t* p, const Wave& w, void* ws, const mu
   g.ws = ws;
   g.inv = reinterpret_cast<const float*>(ws_bytes_ptr(ws, w.inv_off));
   g.sync = nullptr;  // set per phase by run_ns_phase
+  g.sync_every = 0;
   g.a = hp->ns_a;
   g.b = hp->ns_b;
   g.c = hp->ns_c;
@@ -744,7 +749,7 @@ int muon_plan_get_info(const muon_plan_t* plan, muon_plan_info_t* info) {
   }
   info->round_sync_phases = 0;
   for (const Wave& w : plan->waves)
-    for (int ph = 0; ph < 2; ++ph) info->round_sync_phases |= w.sync[ph] ? 1 << ph : 0;
+    for (int ph = 0; ph < 2; ++ph) info->round_sync_phases |= w.sync_every[ph] > 0 ? 1 << ph : 0;
   return MUON_OK;
 }
 
@@ -788,8 +793,10 @@ int run_ns_phase(const muon_plan_t* plan, int32_t wave, void* workspace,
   const int n = static_cast<int>(phase == 3 ? w.bx_count : phase == 2 ? w.aa_count : w.syrk_count);
   muon::GemmArgs g = gemm_args(plan, w, workspace, hp, iter, items);
   g.n_items = n;
-  if (phase != 3 && w.sync[phase - 1])
+  if (phase != 3 && w.sync_every[phase - 1] > 0) {
     g.sync = reinterpret_cast<uint32_t*>(ws_bytes_ptr(workspace, w.sync_off));
+    g.sync_every = w.sync_every[phase - 1];
+  }
   if (fused_params != nullptr) {
     g.params = static_cast<uint16_t*>(fused_params);
     g.clip = clip_of(hp->clip);

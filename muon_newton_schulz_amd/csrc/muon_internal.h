@@ -28,8 +28,10 @@ constexpr int kSplitEdgeMaxTiles = 8;
 constexpr int kSyncGroups = 8;
 constexpr int kSyncStride = 64;  // uint32 elements
 constexpr size_t kSyncBytes = kSyncGroups * kSyncStride * 4;
-// rounds between two holds (each costs a device-scope atomic and polling)
-constexpr int kSyncEvery = 4;
+// rounds between two holds: the plan takes the shortest of 4, 8, 16 and 32
+// that costs little idle time (each hold costs a device-scope atomic and
+// polling; a longer period lets more drift build up between holds)
+constexpr int kSyncEveryMin = 4, kSyncEveryMax = 32;
 
 // Layout of the bf16 NS workspace.  Every matrix there (the iterates X,
 // A and B; all have m_pad rows) is stored as panels of 32 columns: panel q
@@ -115,6 +117,7 @@ struct GemmArgs {
   // per XCD group, kSyncStride apart; zeroed on the stream before each
   // launch that uses them.
   uint32_t* sync;
+  int32_t sync_every;  // rounds between holds (with sync)
 };
 
 // kernel launchers (defined in the .hip files)

@@ -908,11 +908,12 @@ __device__ __forceinline__ void ns_tile(const GemmArgs& g, const MatDev& md, con
 //
 // With GemmArgs::sync set (phases 1 and 2, where the planner finds that a
 // round's tiles cost much the same) the walk also holds each XCD's
-// workgroups together: a workgroup that starts round r (its items are idx = b + r *
-// gridDim.x), r a multiple of kSyncEvery, first waits until the other
-// workgroups of its XCD group have finished round r - 1.  Without it they drift apart by whole tiles over
-// the rounds and read the shared operand panels at different times, from
-// HBM instead of L2.  The wait is a timing device only and is bounded:
+// workgroups together: a workgroup that starts round r (its items are
+// idx = b + r * gridDim.x), r a multiple of GemmArgs::sync_every, first
+// waits until the other workgroups of its XCD group have finished round
+// r - 1.  Without it they drift apart by whole tiles over the rounds and
+// read the shared operand panels at different times, from HBM instead of
+// L2.  The wait is a timing device only and is bounded:
 // after kSyncSpins polls the workgroup goes on (a member of the group may
 // not be resident while other kernels hold CUs).
 constexpr int kSyncSpins = 1024;
@@ -934,13 +935,20 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16(GemmArgs g, const Item* __re
                                                     const float* __restrict__ invs) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * 2 * BT * BK];  // 128 KiB
   bool busy = false;
-  uint32_t* const cnt =
-      g.sync != nullptr ? g.sync + (blockIdx.x % kSyncGroups) * kSyncStride : nullptr;
-  const uint32_t group = gridDim.x / kSyncGroups;
-  uint32_t round = 0;
-  for (int idx = blockIdx.x; idx < g.n_items; idx += gridDim.x, ++round) {
-    if (cnt != nullptr && round > 0 && round % kSyncEvery == 0)
-      xcd_round_barrier(cnt, group * (round / kSyncEvery));
+  // round holds (phases 1 and 2 only): a countdown of the rounds to the
+  // next hold, and the holds passed so far
+  uint32_t* const cnt = PHASE != 3 && g.sync != nullptr
+                            ? g.sync + (blockIdx.x % kSyncGroups) * kSyncStride
+                            : nullptr;
+  int left = g.sync_every;
+  uint32_t holds = 0;
+  for (int idx = blockIdx.x; idx < g.n_items; idx += gridDim.x) {
+    if constexpr (PHASE != 3) {
+      if (cnt != nullptr && idx != static_cast<int>(blockIdx.x) && --left == 0) {
+        left = g.sync_every;
+        xcd_round_barrier(cnt, (gridDim.x / kSyncGroups) * ++holds);
+      }
+    }
     const Item it = items[idx];
     if (it.mat < 0) continue;  // padding of the XCD-grouped order
     const MatDev md = mats[it.mat];
@@ -1095,7 +1103,7 @@ hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
     // round counters (phases 1, 2): on a grid of whole 32-workgroup XCD
     // groups with every workgroup walking the same number of rounds
     GemmArgs a = args;
-    const bool sync = (phase == 1 || phase == 2) && a.sync != nullptr &&
+    const bool sync = (phase == 1 || phase == 2) && a.sync != nullptr && a.sync_every > 0 &&
                       static_cast<int>(grid.x) == kSyncGroups * 32 && n_items > static_cast<int>(grid.x) &&
                       n_items % static_cast<int>(grid.x) == 0;
     if (sync) {
