@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmuon.so")
-SOURCES = ["muon_abi.hip", "elementwise.hip", "ns_gemm.hip", "ns_small.hip", "guard.hip", "clip.hip"]
+SOURCES = ["muon_abi.hip", "elementwise.hip", "ns_gemm.hip", "ns_f32.hip", "ns_small.hip", "guard.hip",
+           "clip.hip"]
 # stand-alone measurement programs: the GPU's sustained bf16 MFMA rate and
 # its HBM stream rates
 PROGRAMS = [("mfma_ceiling", "mfma_ceiling.hip"), ("hbm_ceiling", "hbm_ceiling.hip")]

@@ -139,6 +139,8 @@ hipError_t launch_export(const MatDev* mats, const Item* items, int n_items, int
                          const void* ws, int x_idx, float* out, hipStream_t s);
 hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
                            const GemmArgs& args, hipStream_t s);
+// the fp32 engine's phases (one workgroup per tile item; ns_f32.hip)
+hipError_t launch_ns_f32(int phase, int n_items, const GemmArgs& args, hipStream_t s);
 // n_iter NS iterations (all phases) of each listed small matrix, starting
 // at the iteration args describes
 hipError_t launch_ns_small(int n_mats, const int32_t* list, int n_iter, const GemmArgs& args,

@@ -44,7 +44,7 @@
 // with 16-byte row stores; the symmetric mirror is read back transposed
 // with ds_read_b64_tr_b16 and also written in 16-byte pieces.
 //
-// fp32 engine (tolerance path): 64x64 tiles of plain FMA, same phases.
+// The fp32 engine (the tolerance path) is in ns_f32.hip.
 #include <type_traits>
 
 #include "muon_internal.h"
@@ -987,106 +987,6 @@ __global__ __launch_bounds__(256, 1) void k_ns_bf16_apply(GemmArgs g, const Item
   }
 }
 
-// ------------------------------------------------------------ fp32 engine
-
-constexpr int FT = kTileFp32;  // 64
-constexpr int FK = 16;
-
-template <int PHASE>
-__global__ __launch_bounds__(256) void k_ns_f32(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) float Ps[FK][FT + 4];
-  __shared__ __attribute__((aligned(16))) float Qs[FK][FT + 4];
-  const Item it = g.items[blockIdx.x];
-  if (it.mat < 0) return;  // padding of the XCD-grouped order
-  const MatDev md = g.mats[it.mat];
-  const int ti = it.rc >> 16, tj = it.rc & 0xffff;
-  float* ws = static_cast<float*>(g.ws);
-  const float *P, *Q;
-  int ldp, ldq, K;
-  if (PHASE == 1) {
-    ldp = ldq = K = md.n_pad;
-    P = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(ti) * FT * ldp;
-    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * FT * ldq;
-  } else if (PHASE == 2) {
-    ldp = ldq = K = md.m_pad;
-    P = ws + md.ws_a + static_cast<int64_t>(ti) * FT * ldp;
-    Q = ws + md.ws_a + static_cast<int64_t>(tj) * FT * ldq;
-  } else {
-    ldp = K = md.m_pad;
-    ldq = md.n_pad;
-    P = ws + md.ws_b + static_cast<int64_t>(ti) * FT * ldp;
-    Q = ws + (g.x_cur ? md.ws_x[1] : md.ws_x[0]) + static_cast<int64_t>(tj) * FT;  // [k][j] column block
-  }
-  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-  const int lrow = t >> 2, lk = (t & 3) * 4;      // K-contiguous loads
-  const int qk = t >> 4, qj = (t & 15) * 4;       // [k][j] loads (phase 3)
-  f32x16_t acc = {};
-  for (int k0 = 0; k0 < K; k0 += FK) {
-    const float4 pv = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(lrow) * ldp + k0 + lk);
-    float4 qv;
-    if (PHASE != 3)
-      qv = *reinterpret_cast<const float4*>(Q + static_cast<int64_t>(lrow) * ldq + k0 + lk);
-    else
-      qv = *reinterpret_cast<const float4*>(Q + static_cast<int64_t>(k0 + qk) * ldq + qj);
-    __syncthreads();
-    Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
-    if (PHASE != 3) {
-      Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
-    } else {
-      *reinterpret_cast<float4*>(&Qs[qk][qj]) = qv;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < FK; ++k) {
-      const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(&Ps[k][ty * 4]);
-      const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(&Qs[k][tx * 4]);
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[4 * a + b] = fmaf(p4[a], q4[b], acc[4 * a + b]);
-    }
-  }
-  const float inv = g.first ? g.inv[md.widx] : 1.0f;
-  const int i0 = ti * FT + ty * 4, j0 = tj * FT + tx * 4;
-  f32x16_t v;
-  if (PHASE == 3) {
-    float* X = ws + (g.x_cur ? md.ws_x[0] : md.ws_x[1]);
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-      *reinterpret_cast<float4*>(X + static_cast<int64_t>(i0 + a) * md.n_pad + j0) =
-          make_float4(inv * acc[4 * a], inv * acc[4 * a + 1], inv * acc[4 * a + 2],
-                      inv * acc[4 * a + 3]);
-    return;
-  }
-  const int ldc = md.m_pad;
-  float* C = ws + ((PHASE == 1 && g.c != 0.0f) ? md.ws_a : md.ws_b);
-  const float* Aold = ws + md.ws_a;
-  const float s2 = inv * inv;
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    f32x4_t ao = {0.f, 0.f, 0.f, 0.f};
-    if (PHASE == 2) ao = *reinterpret_cast<const f32x4_t*>(Aold + static_cast<int64_t>(i0 + a) * ldc + j0);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float x;
-      if (PHASE == 1) x = (g.c != 0.0f ? 1.0f : g.b) * s2 * acc[4 * a + b];
-      else x = g.b * ao[b] + g.c * acc[4 * a + b];
-      if ((PHASE == 2 || g.c == 0.0f) && i0 + a == j0 + b) x += g.a;
-      v[4 * a + b] = x;
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-    *reinterpret_cast<float4*>(C + static_cast<int64_t>(i0 + a) * ldc + j0) =
-        make_float4(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
-  if (ti != tj) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      *reinterpret_cast<float4*>(C + static_cast<int64_t>(j0 + b) * ldc + i0) =
-          make_float4(v[b], v[4 + b], v[8 + b], v[12 + b]);
-  }
-}
-
 __global__ void k_zero_u32(uint32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -1121,10 +1021,7 @@ hipError_t launch_ns_phase(int ns_dtype, int phase, int n_items, int n_cu,
     else
       hipLaunchKernelGGL(k_ns_bf16<3>, grid, block, 0, s, a, a.items, a.mats, a.inv);
   } else {
-    const dim3 grid(n_items);
-    if (phase == 1) hipLaunchKernelGGL(k_ns_f32<1>, grid, block, 0, s, args);
-    else if (phase == 2) hipLaunchKernelGGL(k_ns_f32<2>, grid, block, 0, s, args);
-    else hipLaunchKernelGGL(k_ns_f32<3>, grid, block, 0, s, args);
+    return launch_ns_f32(phase, n_items, args, s);
   }
   return hipGetLastError();
 }
