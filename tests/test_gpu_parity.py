@@ -308,15 +308,16 @@ def test_small_matrices_match_oracle(gpu):
     check_muon_step(s, mhp(QUINTIC), tol_w=1e-2)
 
 
-def test_grouped_equals_single_matrix_plans(gpu):
+@pytest.mark.parametrize("ns_dtype,pdt", [("bf16", "bf16"), ("fp32", "fp32")])
+def test_grouped_equals_single_matrix_plans(gpu, ns_dtype, pdt):
     mats, n = _flat([(200, 700), (700, 200), (256, 256), (33, 99)])
-    s = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=5)
+    s = Setup(mats, n, pdt, pdt, ns_dtype, gpu, seed=5)
     P0, G0, M0 = s.params.clone(), s.grads.clone(), s.mom.clone()
     hp = mhp(QUINTIC)
     s.step(hp)
     grouped = s.out.clone()
     for k, m in enumerate(mats):
-        s1 = Setup([m], n, "bf16", "bf16", "bf16", gpu, seed=5)
+        s1 = Setup([m], n, pdt, pdt, ns_dtype, gpu, seed=5)
         s1.params.copy_(P0)
         s1.grads.copy_(G0)
         s1.mom.copy_(M0)
@@ -325,10 +326,11 @@ def test_grouped_equals_single_matrix_plans(gpu):
         assert torch.equal(s1.out[o:o + r * c], grouped[o:o + r * c]), k
 
 
-def test_determinism_waves_and_stage_composition(gpu):
+@pytest.mark.parametrize("ns_dtype,pdt", [("bf16", "bf16"), ("fp32", "fp32")])
+def test_determinism_waves_and_stage_composition(gpu, ns_dtype, pdt):
     mats, n = _flat([(300, 520), (520, 300), (512, 512), (64, 1000), (1000, 64)])
     hp = mhp(QUINTIC)
-    ref = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=9)
+    ref = Setup(mats, n, pdt, pdt, ns_dtype, gpu, seed=9)
     P0, G0, M0 = ref.params.clone(), ref.grads.clone(), ref.mom.clone()
     ref.step(hp)
     results = [(ref.params.clone(), ref.mom.clone(), ref.out.clone())]
@@ -339,15 +341,15 @@ def test_determinism_waves_and_stage_composition(gpu):
     ref.step(hp)
     results.append((ref.params.clone(), ref.mom.clone(), ref.out.clone()))
     # capped workspace -> several waves
-    one = M.muon_workspace_size(mats[:1], n, "bf16", "bf16", "bf16")
-    capped = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=9, cap=2 * one)
+    one = M.muon_workspace_size(mats[:1], n, pdt, pdt, ns_dtype)
+    capped = Setup(mats, n, pdt, pdt, ns_dtype, gpu, seed=9, cap=2 * one)
     assert capped.plan.info().n_waves > 1
     capped.params.copy_(P0)
     capped.mom.copy_(M0)
     capped.step(hp)
     results.append((capped.params.clone(), capped.mom.clone(), capped.out.clone()))
     # stage by stage, through the stage entry points
-    st = Setup(mats, n, "bf16", "bf16", "bf16", gpu, seed=9)
+    st = Setup(mats, n, pdt, pdt, ns_dtype, gpu, seed=9)
     st.params.copy_(P0)
     st.mom.copy_(M0)
     M.muon_stage_momentum(st.plan, 0, G0, st.mom, st.ws, hp)
