@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X fp32 matrix
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -117,6 +118,8 @@ def parse():
                     help="fp64 NS flops of the oracle's CPU sample (about 10 s on 16 cores)")
     ap.add_argument("--no-parity", action="store_true",
                     help="skip the oracle checks of the first and last step")
+    ap.add_argument("--no-fp32-ns", action="store_true",
+                    help="skip the timing of the fp32 NS engine on one dense layer")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the MFMA and HBM ceiling programs (profiling runs)")
     ap.add_argument("--adamw-stream", choices=["same", "side"], default="side",
@@ -618,6 +621,32 @@ def main():
                      "max_logit_per_head_all_clipped": entry(per_head, 2)}
         del fplan, hplan
 
+    # ---- the fp32 NS engine (the 1e-4 tolerance path), timed apart on one
+    # dense layer's seven matrices in fp32 (4 x 2048^2, 2 x 2048x5632,
+    # 5632x2048; seeded N(0, 0.02^2) weights and gradients): muon_step with
+    # fp32 NS, against the fp32 matrix-core peak
+    ns_fp32 = None
+    if not args.no_fp32_ns:
+        f_shapes = [(2048, 2048)] * 4 + [(2048, 5632)] * 2 + [(5632, 2048)]
+        f_mats, f_n = [], 0
+        for r_, c_ in f_shapes:
+            f_mats.append((f_n, r_, c_))
+            f_n += r_ * c_
+        fg = torch.Generator(device=dev)
+        fg.manual_seed(W.seed_key(wl.config_id, 9, 0, 0))
+        f_p = torch.randn(f_n, generator=fg, device=dev) * 0.02
+        f_g = torch.randn(f_n, generator=fg, device=dev) * 0.02
+        f_m = torch.zeros(f_n, device=dev)
+        f_plan = M.muon_plan_create(f_mats, f_n, "fp32", "fp32", "fp32")
+        f_ws = f_plan.alloc_workspace(dev)
+        f_ms = time_launch(lambda: M.muon_step(f_plan, f_p, f_g, f_m, f_ws, hp), reps=3)
+        f_fl = sum(W.ns_flops_matrix(r_, c_, hp.ns_steps, hp.ns_c) for r_, c_ in f_shapes)
+        ns_fp32 = {"matrices": "4 x 2048x2048, 2 x 2048x5632, 5632x2048 (fp32)",
+                   "ns_flops": f_fl, "ms_per_step": f_ms,
+                   "tflops": f_fl / (f_ms * 1e-3) / 1e12,
+                   "frac_of_fp32_mfma_peak": f_fl / (f_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
+        del f_plan, f_ws, f_p, f_g, f_m
+
     ceiling = None if args.no_ceilings else run_ceiling("mfma_ceiling")
     hbm_ceiling = None if args.no_ceilings else run_ceiling("hbm_ceiling")
 
@@ -729,6 +758,8 @@ def main():
         # MuonClip over the stack's W_q / W_k, timed apart (bytes: read once
         # for the norm, read + write when a block is rescaled)
         "muon_clip": muon_clip,
+        # the fp32 NS engine (tolerance path), timed apart on a dense layer
+        "ns_fp32_engine": ns_fp32,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, hp, args.cpu_flops, 1 << 23)
